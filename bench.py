@@ -1,0 +1,187 @@
+"""Benchmark of the attention forward hot path on one MI355X.
+
+One step = one pass of the whole path over synthetic inputs already resident
+in HBM:
+  * prefill: causal bf16 attention, B=1, H=32, N=16384, d=128 (fa_fwd);
+  * decode: paged GQA decode, 64 sequences with KV lengths U[512, 32768]
+    (seed 4), page size 16, 32 query / 8 KV heads, d=128 (fa_decode_paged).
+``value`` is the prefill throughput in TFLOP/s (4*B*H*N^2*d/2 per call);
+the decode line reports KV bytes read per second. Each call is timed with
+HIP events on the stream it is launched on; ``ms_per_step`` is the wall
+time of the timed steps divided by their number.
+
+The CPU baseline is the fp64 oracle run on a bounded sample of the same
+prefill workload (whole heads, every row) on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (prefill) & KV GB/s (paged decode), % of MI355X peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(x, heads: int):
+    """fp64 oracle on `heads` whole heads of the prefill workload."""
+    import numpy as np
+
+    import fa_inputs as fi
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    B, Nq, Nk, Hq, Hkv, d = x.shape
+    t0 = time.perf_counter()
+    for h in range(heads):
+        qh = fi.to_f64(x.q[0, :, h], "bf16")
+        kh = fi.to_f64(x.k[0, :, h], "bf16")
+        vh = fi.to_f64(x.v[0, :, h], "bf16")
+        oracle.attention_head(qh, kh, vh, x.scale, True)
+    dt = time.perf_counter() - t0
+    flops = fi.prefill_flops([Nq], [Nk], heads, d, True)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of 32 heads of the causal N=16384 d=128 prefill, all rows, "
+                      f"fp64 NumPy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              f"(this build runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fa_inputs as fi
+    import io_aware_exact_flashattention_amd as fa
+    from tests.util import to_dev
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    do_pre = args.only in ("prefill", "both")
+    do_dec = args.only in ("decode", "both")
+
+    log("[bench] generating prefill inputs")
+    x = fi.cfg2()
+    B, Nq, Nk, Hq, Hkv, d = x.shape
+    pre_flops = fi.prefill_flops([Nq] * B, [Nk] * B, Hq, d, True)
+    if do_pre:
+        q, k, v = to_dev(x.q, "bf16"), to_dev(x.k, "bf16"), to_dev(x.v, "bf16")
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Nq, Hq), dtype=torch.float32, device=dev)
+
+    if do_dec:
+        log("[bench] generating decode inputs")
+        p = fi.cfg4()
+        dq, dkp, dvp = to_dev(p.q, "bf16"), to_dev(p.k_pool, "bf16"), to_dev(p.v_pool, "bf16")
+        dpt, dsl = to_dev(p.page_table, "i32"), to_dev(p.seq_lens, "i32")
+        kv_bytes = fi.decode_kv_bytes(p.seq_lens, p.k_pool.shape[2], p.k_pool.shape[3], "bf16")
+        Bd, Hqd, dd = p.q.shape
+        ws = torch.empty(fa.decode_workspace_size(Bd, Hqd, dd, p.max_pages), dtype=torch.uint8,
+                         device=dev)
+        do_ = torch.empty_like(dq)
+        dl = torch.empty((Bd, Hqd), dtype=torch.float32, device=dev)
+        del p.k_seq, p.v_seq
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if do_pre:
+            if ev is not None:
+                ev[0].record(stream)
+            fa.fwd(q, k, v, causal=True, scale=x.scale, out=o, lse=lse)
+            if ev is not None:
+                ev[1].record(stream)
+        if do_dec:
+            if ev is not None:
+                ev[2].record(stream)
+            fa.decode_paged(dq, dkp, dvp, dpt, dsl, scale=p.scale, workspace=ws, out=do_, lse=dl)
+            if ev is not None:
+                ev[3].record(stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = [e[0].elapsed_time(e[1]) for e in events] if do_pre else []
+    dec_ms = [e[2].elapsed_time(e[3]) for e in events] if do_dec else []
+    out = {
+        "metric": METRIC,
+        "value": None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal bf16 prefill B=1 H=32 N=16384 d=128 (fa_fwd) + paged GQA decode "
+                        "64 seqs KV U[512,32768] seed 4, page 16, Hq=32 Hkv=8 d=128 (fa_decode_paged)",
+            "prefill": {"B": B, "N": Nq, "H": Hq, "d": d, "causal": True, "flops_per_call": pre_flops},
+        },
+    }
+    if do_pre:
+        avg = float(np.mean(pre_ms))
+        tflops = pre_flops / (avg * 1e-3) / 1e12
+        out["value"] = tflops
+        out["prefill_ms"] = {"mean": avg, "median": float(np.median(pre_ms)), "min": float(np.min(pre_ms))}
+        out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                           "kernel": "fwd_mfma_kernel<Bf16,128,causal>"}
+    if do_dec:
+        avg = float(np.mean(dec_ms))
+        gbs = kv_bytes / (avg * 1e-3) / 1e9
+        out["decode"] = {
+            "value": gbs, "unit": "GB/s", "kv_bytes_per_call": kv_bytes,
+            "ms": {"mean": avg, "median": float(np.median(dec_ms)), "min": float(np.min(dec_ms))},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                         "kernel": "decode_split_kernel + decode_combine_kernel"},
+        }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle)")
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,135 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * Every entry point computes exact attention, O = softmax(scale * Q K^T) V,
+ * row by row, plus the natural-log log-sum-exp of each row's scaled logits.
+ * The kernels follow the fused forward pass described on the page
+ * "I/O-Aware Kernels" (datasystem.school, Module 5), section "FlashAttention:
+ * tiling + online softmax": one on-chip Q tile streams K/V tiles, keeps a
+ * running row max m and sum l, and rescales its output accumulator, so the
+ * score matrix is never written to device memory. The serving variants
+ * (ragged batches, grouped-query heads, K/V gathered from a paged cache) are
+ * those of section "FlashInfer: I/O-aware attention for serving".
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor pointers are DEVICE pointers on the current HIP device,
+ *   allocated and owned by the caller. The library never allocates, frees
+ *   or synchronises; each call enqueues one or two kernels on `stream` (a
+ *   hipStream_t passed as void*, NULL = the null stream) and returns.
+ * - Tensors are dense and contiguous in the layouts stated per call, with
+ *   the element type `dtype` (O has the type of Q). LSE is always float32.
+ *   Q/K/V/O/pool pointers must be 16-byte aligned.
+ * - `scale` multiplies Q K^T before the softmax; it must be finite and > 0
+ *   (1/sqrt(d) is the usual value).
+ * - Head dimension d must be 64 or 128.
+ * - Grouped-query attention: Hq must be a multiple of Hkv and query head h
+ *   reads key/value head h / (Hq / Hkv).
+ * - Causal masking is aligned bottom-right: query row i of a sequence with
+ *   Lq queries and Lk keys sees key j iff j <= i + (Lk - Lq). A row that sees
+ *   no key gets O = 0 and LSE = -inf.
+ * - Arguments are validated on the host before any HIP call; on an invalid
+ *   argument nothing is launched and outputs are untouched. Index arrays
+ *   that live on the device (cu_seqlens, page_table, seq_lens) are trusted:
+ *   out-of-range contents are undefined behaviour.
+ * - Calls keep no state between them and may be issued from several host
+ *   threads; calls on different streams that write the same outputs race.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad scale, Hq % Hkv != 0, small workspace */
+  FA_ERR_UNSUPPORTED = 2, /* valid request outside what is built: d, page size, dtype for a call */
+  FA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+/* Human-readable text for a status code (static storage). */
+const char* fa_status_string(fa_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+/*
+ * fa_fwd - dense batch, optional causal mask.
+ * ("I/O-Aware Kernels", section "FlashAttention: tiling + online softmax".)
+ *   q   [B, Nq, Hq, d]     dtype
+ *   k,v [B, Nk, Hkv, d]    dtype
+ *   o   [B, Nq, Hq, d]     dtype (written)
+ *   lse [B, Nq, Hq]        float32 (written), natural log
+ * B, Nq, Nk, Hq, Hkv >= 1. dtype FA_F32, FA_F16 or FA_BF16.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Nq, int Nk, int Hq, int Hkv, int d, fa_dtype dtype,
+                 float scale, int causal, void* stream);
+
+/*
+ * fa_fwd_varlen - packed ragged batch of B sequences.
+ * ("I/O-Aware Kernels", section "FlashInfer: I/O-aware attention for
+ * serving": ragged, variable-length batches, multi-head and grouped-query.)
+ *   q   [Tq, Hq, d], k/v [Tk, Hkv, d], o [Tq, Hq, d]   dtype
+ *   lse [Tq, Hq] float32
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [B+1], cu[0] = 0, non-decreasing,
+ *     cu_q[B] = Tq, cu_k[B] = Tk; sequence s owns rows cu[s] .. cu[s+1]-1.
+ *   max_seqlen_q >= every query length (sizes the grid); max_seqlen_k is
+ *     accepted for interface symmetry and only checked for sign.
+ * Sequences may be empty. B >= 1, Tq, Tk >= 0.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                        int max_seqlen_q, int max_seqlen_k, int Tq, int Tk, int Hq, int Hkv,
+                        int d, fa_dtype dtype, float scale, int causal, void* stream);
+
+/*
+ * fa_decode_paged_workspace_size - bytes of device workspace that
+ * fa_decode_paged needs for these sizes (float32 partial outputs and
+ * log-sum-exps of every split). Returns 0 for invalid sizes.
+ */
+size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_pages, int page_size,
+                                      int num_splits);
+
+/*
+ * fa_decode_paged - one query token per sequence against K/V gathered from
+ * a paged cache through a page table, split over the key axis and merged
+ * with a log-sum-exp combine pass.
+ * ("I/O-Aware Kernels", section "FlashInfer: I/O-aware attention for
+ * serving": paged KV layouts, grouped-query attention.)
+ *   q          [B, Hq, d]                      dtype
+ *   k_pool,v_pool [num_pages, page_size, Hkv, d] dtype: page p, slot t holds
+ *              the key/value of one token for every KV head
+ *   page_table device int32 [B, max_pages]: entry i of sequence b is the
+ *              physical page holding its tokens 16*i .. 16*i+15; entries at
+ *              or beyond ceil(seq_lens[b]/page_size) are not read
+ *   seq_lens   device int32 [B], 0 <= seq_lens[b] <= max_pages*page_size
+ *   o [B, Hq, d] dtype, lse [B, Hq] float32 (written)
+ *   num_splits 0 = automatic (32 pages per split), else the number of key
+ *              splits of the longest sequence (1 .. max_pages)
+ *   workspace  device buffer of at least
+ *              fa_decode_paged_workspace_size(B, Hq, d, max_pages, page_size,
+ *              num_splits) bytes, owned by the caller; its contents are
+ *              scratch (overwritten, not read before written).
+ * page_size must be 16. The query is the last token of its sequence, so it
+ * sees every key; slots of a last page beyond seq_lens are never read into
+ * the result (their contents, even NaN, do not matter).
+ */
+fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool, void* o,
+                          float* lse, const int32_t* page_table, const int32_t* seq_lens, int B,
+                          int max_pages, int num_pages, int page_size, int Hq, int Hkv, int d,
+                          fa_dtype dtype, float scale, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,148 @@
+"""MI355X (gfx950) exact attention forward: Python binding of libfa_amd.so.
+
+Three entry points, each returning (O, LSE) and each one call into the C ABI
+(include/fa.h), enqueued on torch's current HIP stream:
+
+* ``fwd(q, k, v, causal=False, scale=None)`` - dense [B, N, H, d];
+* ``fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, ...)`` -
+  packed ragged [T, H, d];
+* ``decode_paged(q, k_pool, v_pool, page_table, seq_lens, ...)`` - one token
+  per sequence against a paged K/V cache.
+
+PyTorch only allocates device memory and supplies the stream; the arithmetic
+runs in the library's kernels. There is no CPU or PyTorch fallback: on a
+machine without the built library every call raises.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import FaError
+
+__all__ = ["fwd", "fwd_varlen", "decode_paged", "decode_workspace_size", "FaError",
+           "default_scale"]
+
+_DT = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d) rounded to float32, the value the library receives."""
+    import struct
+    return struct.unpack("f", struct.pack("f", 1.0 / math.sqrt(d)))[0]
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev_tensor(t: torch.Tensor, name: str):
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.is_cuda, f"{name} must be on the GPU")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+        scale: float | None = None, out: torch.Tensor | None = None,
+        lse: torch.Tensor | None = None):
+    """Dense attention. q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] -> (O like q,
+    LSE float32 [B, Nq, Hq])."""
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(t, n)
+    _need(q.dim() == 4 and k.dim() == 4 and k.shape == v.shape, "bad shapes")
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, dk = k.shape
+    _need(k.shape[0] == B and dk == d, "k/v must match q in batch and head dim")
+    if scale is None:
+        scale = default_scale(d)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o.shape == q.shape and o.dtype == q.dtype and o.is_contiguous(), "bad out")
+    _need(l.shape == (B, Nq, Hq) and l.dtype == torch.float32 and l.is_contiguous(), "bad lse")
+    _lib.check(lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                          B, Nq, Nk, Hq, Hkv, d, _dtype(q), float(scale), int(bool(causal)),
+                          _stream(q)))
+    return o, l
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+               cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+               causal: bool = False, scale: float | None = None,
+               out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Packed ragged batch. q [Tq, Hq, d], k/v [Tk, Hkv, d], cu_seqlens int32
+    [B+1] on the GPU -> (O like q, LSE float32 [Tq, Hq])."""
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q),
+                 ("cu_seqlens_k", cu_seqlens_k)):
+        _dev_tensor(t, n)
+    _need(q.dim() == 3 and k.dim() == 3 and k.shape == v.shape, "bad shapes")
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32,
+          "cu_seqlens must be int32")
+    _need(cu_seqlens_q.shape == cu_seqlens_k.shape and cu_seqlens_q.dim() == 1, "bad cu_seqlens")
+    Tq, Hq, d = q.shape
+    Tk, Hkv, _ = k.shape
+    B = cu_seqlens_q.shape[0] - 1
+    if scale is None:
+        scale = default_scale(d)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _lib.check(lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 l.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                                 B, int(max_seqlen_q), int(max_seqlen_k), Tq, Tk, Hq, Hkv, d,
+                                 _dtype(q), float(scale), int(bool(causal)), _stream(q)))
+    return o, l
+
+
+def decode_workspace_size(B: int, Hq: int, d: int, max_pages: int, page_size: int = 16,
+                          num_splits: int = 0) -> int:
+    return int(_lib.load().fa_decode_paged_workspace_size(B, Hq, d, max_pages, page_size,
+                                                          num_splits))
+
+
+def decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                 page_table: torch.Tensor, seq_lens: torch.Tensor, num_splits: int = 0,
+                 scale: float | None = None, workspace: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Paged decode. q [B, Hq, d]; pools [num_pages, 16, Hkv, d]; page_table
+    int32 [B, max_pages]; seq_lens int32 [B] -> (O like q, LSE float32 [B, Hq])."""
+    lib = _lib.load()
+    for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("page_table", page_table),
+                 ("seq_lens", seq_lens)):
+        _dev_tensor(t, n)
+    _need(q.dim() == 3 and k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "bad shapes")
+    _need(q.dtype == k_pool.dtype == v_pool.dtype, "q and pools must share a dtype")
+    _need(page_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "indices must be int32")
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv, _ = k_pool.shape
+    max_pages = page_table.shape[1]
+    _need(page_table.shape[0] == B and seq_lens.shape == (B,), "bad index shapes")
+    if scale is None:
+        scale = default_scale(d)
+    need = int(lib.fa_decode_paged_workspace_size(B, Hq, d, max_pages, page_size, num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _lib.check(lib.fa_decode_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                   o.data_ptr(), l.data_ptr(), page_table.data_ptr(),
+                                   seq_lens.data_ptr(), B, max_pages, num_pages, page_size, Hq,
+                                   Hkv, d, _dtype(q), float(scale), int(num_splits),
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream(q)))
+    return o, l

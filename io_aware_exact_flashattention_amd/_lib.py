@@ -1,0 +1,62 @@
+"""ctypes binding of ``libfa_amd.so`` (the C ABI declared in include/fa.h).
+
+Argument marshalling only: every arithmetic step runs in the library's HIP
+kernels. Loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa_amd.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+
+EXPORTS = ("fa_status_string", "fa_version", "fa_fwd", "fa_fwd_varlen",
+           "fa_decode_paged_workspace_size", "fa_decode_paged")
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+_SIGNATURES = {
+    "fa_status_string": (ctypes.c_char_p, [_i]),
+    "fa_version": (_i, []),
+    "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "fa_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                           _i, _f, _i, _vp]),
+    "fa_decode_paged_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                             _f, _i, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library (once). Raises if it is missing: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m io_aware_exact_flashattention_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != FA_OK:
+        raise FaError(status, load().fa_status_string(status).decode())

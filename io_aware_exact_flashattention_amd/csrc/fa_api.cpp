@@ -1,0 +1,154 @@
+// fa_api.cpp - the C ABI: host-side argument validation, grid sizing and
+// dispatch to the gfx950 kernels. Validation happens before any HIP call,
+// so an invalid request launches nothing and touches no output.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kPageSize = 16;
+constexpr int kAutoPagesPerSplit = 32;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+fa_status check_common(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, int Hq, int Hkv, int d, fa_dtype dt, float scale) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (dt != FA_F32 && dt != FA_F16 && dt != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (Hq <= 0 || Hkv <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID_ARG;
+  if (!head_dim_ok(d)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+fa::Dt to_dt(fa_dtype t) {
+  return t == FA_F32 ? fa::Dt::F32 : t == FA_F16 ? fa::Dt::F16 : fa::Dt::Bf16;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+fa_status run_fwd(fa::FwdParams& p, fa_dtype dt, int d, int causal, int max_q, void* stream) {
+  const int bm = fa::fwd_block_rows(to_dt(dt));
+  p.n_qtiles = (max_q + bm - 1) / bm;
+  const int64_t blocks = (int64_t)p.n_qtiles * p.Hq * p.B;
+  if (blocks == 0) return FA_OK;  // nothing to compute
+  if (blocks > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_fwd(p, to_dt(dt), d, causal != 0, (int)blocks, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error at launch";
+  }
+  return "unknown fa_status";
+}
+
+int fa_version(void) { return 100; }
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq,
+                 int Nk, int Hq, int Hkv, int d, fa_dtype dtype, float scale, int causal,
+                 void* stream) {
+  fa_status st = check_common(q, k, v, o, lse, Hq, Hkv, d, dtype, scale);
+  if (st != FA_OK) return st;
+  if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_INVALID_ARG;
+  if ((int64_t)B * Nq > INT32_MAX || (int64_t)B * Nk > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  fa::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.cu_q = nullptr; p.cu_k = nullptr;
+  p.B = B; p.Nq = Nq; p.Nk = Nk;
+  p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.scale_log2 = scale * kLog2e;
+  p.q_row = (int64_t)Hq * d;
+  p.kv_row = (int64_t)Hkv * d;
+  return run_fwd(p, dtype, d, causal, Nq, stream);
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                        int max_seqlen_q, int max_seqlen_k, int Tq, int Tk, int Hq, int Hkv,
+                        int d, fa_dtype dtype, float scale, int causal, void* stream) {
+  fa_status st = check_common(q, k, v, o, lse, Hq, Hkv, d, dtype, scale);
+  if (st != FA_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || Tq < 0 || Tk < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return FA_ERR_INVALID_ARG;
+  if (max_seqlen_q > Tq) return FA_ERR_INVALID_ARG;
+  if (Tq == 0 || max_seqlen_q == 0) return FA_OK;  // no query rows
+  fa::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+  p.B = B; p.Nq = 0; p.Nk = 0;
+  p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.scale_log2 = scale * kLog2e;
+  p.q_row = (int64_t)Hq * d;
+  p.kv_row = (int64_t)Hkv * d;
+  return run_fwd(p, dtype, d, causal, max_seqlen_q, stream);
+}
+
+static int pages_per_split(int max_pages, int num_splits) {
+  if (num_splits <= 0) return kAutoPagesPerSplit;
+  return (max_pages + num_splits - 1) / num_splits;
+}
+
+size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_pages, int page_size,
+                                      int num_splits) {
+  if (B <= 0 || Hq <= 0 || d <= 0 || max_pages <= 0 || page_size <= 0 || num_splits < 0)
+    return 0;
+  if (num_splits > max_pages) return 0;
+  const int pps = pages_per_split(max_pages, num_splits);
+  const int64_t splits = (max_pages + pps - 1) / pps;
+  return (size_t)B * Hq * splits * ((size_t)d + 1) * sizeof(float);
+}
+
+fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool, void* o,
+                          float* lse, const int32_t* page_table, const int32_t* seq_lens, int B,
+                          int max_pages, int num_pages, int page_size, int Hq, int Hkv, int d,
+                          fa_dtype dtype, float scale, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  fa_status st = check_common(q, k_pool, v_pool, o, lse, Hq, Hkv, d, dtype, scale);
+  if (st != FA_OK) return st;
+  if (!page_table || !seq_lens || !workspace) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || max_pages <= 0 || num_pages <= 0 || page_size <= 0) return FA_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > max_pages) return FA_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  if (page_size != kPageSize) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_decode_paged_workspace_size(B, Hq, d, max_pages, page_size, num_splits);
+  if (need == 0 || workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  const int pps = pages_per_split(max_pages, num_splits);
+  const int splits = (max_pages + pps - 1) / pps;
+  if ((int64_t)splits > 65535 * 16 || (int64_t)Hkv * Hq > 65535 || B > 65535)
+    return FA_ERR_UNSUPPORTED;
+
+  fa::DecodeParams p{};
+  p.q = q; p.k_pool = k_pool; p.v_pool = v_pool; p.o = o; p.lse = lse;
+  p.page_table = page_table; p.seq_lens = seq_lens;
+  p.B = B; p.max_pages = max_pages; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.pages_per_split = pps;
+  p.max_splits = splits;
+  p.scale_log2 = scale * kLog2e;
+  float* ws = static_cast<float*>(workspace);
+  p.o_part = ws;
+  p.lse_part = ws + (size_t)B * Hq * splits * d;
+  hipError_t e = fa::launch_decode(p, to_dt(dtype), d, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// fa_device.h - device-side helpers shared by the gfx950 attention kernels:
+// vector types, MFMA wrappers, 16-bit <-> float conversion and LDS swizzles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element-type tags. Storage on the device is 16-bit raw bits for both
+// half types; the tag selects the MFMA and the conversions.
+struct Bf16 {};
+struct F16 {};
+
+template <typename T> struct Elem;
+
+template <> struct Elem<Bf16> {
+  // D(32x32, f32) += A(32x16) * B(16x32); 8 bf16 per lane per operand.
+  __device__ static __forceinline__ f32x16 mma32(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // Two floats -> two bf16 (round to nearest even), low half = lo.
+  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static __forceinline__ float lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+  __device__ static __forceinline__ float hi(uint32_t w) {
+    return __builtin_bit_cast(float, w & 0xffff0000u);
+  }
+};
+
+template <> struct Elem<F16> {
+  __device__ static __forceinline__ f32x16 mma32(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  __device__ static __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Lane value exchange within a wavefront (64 lanes).
+__device__ __forceinline__ float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Byte-select of two 32-bit words (v_perm_b32): result byte i is byte
+// sel[i] of the 8-byte value (hi:lo).
+__device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+}  // namespace fa

@@ -1,0 +1,56 @@
+// fa_internal.h - parameter blocks and launchers shared between the C ABI
+// (fa_api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Prefill (dense or ragged). Tokens of every tensor are rows of a packed
+// [T, H, d] view; a dense [B, N, H, d] tensor is the ragged case with
+// sequence s starting at row s * N. cu_q / cu_k are null for dense calls.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int B;
+  int Nq, Nk;        // dense lengths (unused when cu_q != null)
+  int Hq, Hkv, group;
+  int n_qtiles;      // query tiles of the longest sequence
+  float scale_log2;  // scale * log2(e)
+  int64_t q_row;     // elements between consecutive tokens of q and o (Hq * d)
+  int64_t kv_row;    // elements between consecutive tokens of k and v (Hkv * d)
+};
+
+// Split-KV decode over a paged cache.
+struct DecodeParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  void* o;
+  float* lse;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  float* o_part;      // [B, Hq, max_splits, d]
+  float* lse_part;    // [B, Hq, max_splits]
+  int B, max_pages, Hq, Hkv, group;
+  int pages_per_split;
+  int max_splits;
+  float scale_log2;
+};
+
+enum class Dt { F32, F16, Bf16 };
+
+// Each launcher enqueues its kernel(s) on `stream` and returns hipGetLastError().
+hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, int grid_blocks,
+                      hipStream_t stream);
+int fwd_block_rows(Dt dt);  // query rows per workgroup for this dtype
+
+hipError_t launch_decode(const DecodeParams& p, Dt dt, int d, hipStream_t stream);
+
+}  // namespace fa

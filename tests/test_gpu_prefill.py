@@ -1,0 +1,190 @@
+"""GPU parity of the prefill entry points (fa_fwd, fa_fwd_varlen) against
+the fp64 CPU oracle, plus bitwise structural checks. Every call goes
+through the C ABI via the Python binding."""
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+import oracle
+from tests.util import assert_parity, dense_dev, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+fa = pytest.importorskip("io_aware_exact_flashattention_amd")
+
+
+def run_dense(x: fi.Dense):
+    q, k, v = dense_dev(x)
+    o, l = fa.fwd(q, k, v, causal=x.causal, scale=x.scale)
+    torch.cuda.synchronize()
+    return to_f64(o), to_f64(l)
+
+
+def check_dense_full(x: fi.Dense, what):
+    print(f"[case] {what} shape={x.shape} dtype={x.dtype} causal={x.causal}", flush=True)
+    o, l = run_dense(x)
+    O, L = oracle.attention(fi.to_f64(x.q, x.dtype), fi.to_f64(x.k, x.dtype),
+                            fi.to_f64(x.v, x.dtype), x.scale, x.causal)
+    return assert_parity(o, l, O, L, fi.to_f64(x.v, x.dtype), x.dtype, what)
+
+
+def test_cfg0_fp32_single_head():
+    check_dense_full(fi.cfg0(), "cfg0 fp32 B1 H1 N256 d64")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(300, 300), (200, 333), (333, 200), (1, 77), (64, 64), (129, 5)])
+def test_dense_small_ragged(dtype, d, causal, nq, nk):
+    x = fi.dense(2, nq, nk, 4, 2, d, dtype, seed=100 + nq + nk + d, causal=causal)
+    check_dense_full(x, f"dense {dtype} d{d} causal={causal} nq={nq} nk={nk}")
+
+
+@pytest.mark.parametrize("dtype,q_mult", [("bf16", 1.0), ("bf16", 8.0), ("f16", 1.0)])
+def test_cfg1_causal_multihead(dtype, q_mult):
+    x = fi.cfg1(dtype=dtype, q_mult=q_mult)
+    if q_mult != 1.0:
+        qk = fi.to_f64(x.q[0, :256, 0], dtype) @ fi.to_f64(x.k[0, :, 0], dtype).T * x.scale
+        print(f"[info] stability variant: max|logit| on a 256-row sample = {np.abs(qk).max():.1f}")
+    check_dense_full(x, f"cfg1 {dtype} qx{q_mult:g}")
+
+
+def test_cfg2_long_context_sampled_rows():
+    """Full size B=1 H=32 N=16384 d=128 causal bf16: oracle on sampled rows
+    (each row's full score row), in the launch configuration of the bench."""
+    x = fi.cfg2()
+    print(f"[case] cfg2 sampled rows", flush=True)
+    o, l = run_dense(x)
+    rng = np.random.default_rng(1234)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 16383], rng.integers(0, 16384, 27)]))
+    heads = [0, 7, 19, 31]
+    errs = []
+    vmax = np.abs(fi.to_f64(x.v, "bf16")).max()
+    for h in heads:
+        kh = fi.to_f64(x.k[0, :, h], "bf16")
+        vh = fi.to_f64(x.v[0, :, h], "bf16")
+        O, L = oracle.attention_rows(fi.to_f64(x.q[0, rows, h], "bf16"), rows, 16384, kh, vh,
+                                     x.scale, True)
+        assert_parity(o[0, rows, h], l[0, rows, h], O, L, np.array([vmax]), "bf16", f"cfg2 head {h}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+def test_cfg2_closed_form_zero_q():
+    """Q = 0 at full size: row i of a causal call is the mean of V[0..i] and
+    its LSE is ln(i+1) - an O(N d) check of every output row."""
+    x = fi.cfg2()
+    x.q[...] = 0
+    q, k, v = dense_dev(x)
+    o, l = fa.fwd(q, k, v, causal=True, scale=x.scale)
+    # prefix means in float64 on the host
+    vv = fi.to_f64(x.v[0], "bf16")                                  # [N, H, d]
+    pref = np.cumsum(vv, axis=0) / np.arange(1, 16385)[:, None, None]
+    og = to_f64(o)[0]
+    err = np.abs(og - pref).max() / np.abs(vv).max()
+    lerr = np.abs(to_f64(l)[0] - np.log(np.arange(1, 16385))[:, None]).max()
+    print(f"[parity] cfg2 Q=0 closed form: err_O={err:.3e} err_LSE={lerr:.3e}")
+    assert err <= 1e-2 and lerr <= 1e-4 * np.log(16384)
+
+
+def check_varlen(x: fi.Varlen, what, sample_rows=None):
+    print(f"[case] {what}", flush=True)
+    q, k, v = to_dev(x.q, x.dtype), to_dev(x.k, x.dtype), to_dev(x.v, x.dtype)
+    cq, ck = to_dev(x.cu_q, "i32"), to_dev(x.cu_k, "i32")
+    o, l = fa.fwd_varlen(q, k, v, cq, ck, x.max_q, x.max_k, causal=x.causal, scale=x.scale)
+    torch.cuda.synchronize()
+    o, l = to_f64(o), to_f64(l)
+    assert np.all(np.isfinite(o))
+    if sample_rows is None:
+        O, L = oracle.attention_varlen(fi.to_f64(x.q, x.dtype), fi.to_f64(x.k, x.dtype),
+                                       fi.to_f64(x.v, x.dtype), x.cu_q, x.cu_k, x.scale, x.causal)
+        return assert_parity(o, l, O, L, fi.to_f64(x.v, x.dtype), x.dtype, what)
+    rng = np.random.default_rng(99)
+    Hq, Hkv = x.q.shape[1], x.k.shape[1]
+    vmax = np.abs(fi.to_f64(x.v, x.dtype)).max()
+    for s in range(len(x.cu_q) - 1):
+        a, b, c, e = (int(t) for t in (x.cu_q[s], x.cu_q[s + 1], x.cu_k[s], x.cu_k[s + 1]))
+        if b == a:
+            continue
+        rows = np.unique(np.concatenate([[0, b - a - 1], rng.integers(0, b - a, sample_rows)]))
+        for h in (0, Hq // 2 + 1, Hq - 1):
+            g = oracle.kv_head_of(h, Hq, Hkv)
+            O, L = oracle.attention_rows(fi.to_f64(x.q[a + rows, h], x.dtype), rows, b - a,
+                                         fi.to_f64(x.k[c:e, g], x.dtype),
+                                         fi.to_f64(x.v[c:e, g], x.dtype), x.scale, x.causal)
+            assert_parity(o[a + rows, h], l[a + rows, h], O, L, np.array([vmax]), x.dtype,
+                          f"{what} seq {s} head {h}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_small_with_empty_sequences(dtype, causal):
+    lq = [130, 0, 1, 64, 257, 3]
+    lk = [130, 5, 1, 100, 257, 0]
+    x = fi.varlen(lq, lk, 8, 2, 128, dtype, seed=31, causal=causal)
+    check_varlen(x, f"varlen small {dtype} causal={causal}")
+
+
+def test_cfg3_varlen_gqa_sampled():
+    check_varlen(fi.cfg3(), "cfg3 varlen GQA", sample_rows=24)
+
+
+# ------------------------------------------------------------ bitwise --
+def test_varlen_slice_equals_dense_bitwise():
+    x = fi.cfg3()
+    q, k, v = to_dev(x.q, "bf16"), to_dev(x.k, "bf16"), to_dev(x.v, "bf16")
+    o, l = fa.fwd_varlen(q, k, v, to_dev(x.cu_q, "i32"), to_dev(x.cu_k, "i32"), x.max_q, x.max_k,
+                         causal=True)
+    for s in (1, 6):
+        a, b = int(x.cu_q[s]), int(x.cu_q[s + 1])
+        od, ld = fa.fwd(q[a:b][None].contiguous(), k[a:b][None].contiguous(),
+                        v[a:b][None].contiguous(), causal=True)
+        assert torch.equal(od[0], o[a:b]) and torch.equal(ld[0], l[a:b])
+
+
+def test_gqa_equals_repeated_heads_bitwise():
+    x = fi.dense(2, 300, 300, 8, 2, 128, "bf16", seed=5, causal=True)
+    q, k, v = dense_dev(x)
+    o1, l1 = fa.fwd(q, k, v, causal=True)
+    o2, l2 = fa.fwd(q, k.repeat_interleave(4, dim=2).contiguous(),
+                    v.repeat_interleave(4, dim=2).contiguous(), causal=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_deterministic_and_every_row_written():
+    x = fi.dense(1, 1000, 1000, 4, 4, 64, "bf16", seed=6, causal=True)
+    q, k, v = dense_dev(x)
+    o1 = torch.full_like(q, float("nan"))
+    l1 = torch.full((1, 1000, 4), float("nan"), device="cuda")
+    fa.fwd(q, k, v, causal=True, out=o1, lse=l1)
+    o2, l2 = fa.fwd(q, k, v, causal=True)
+    assert not torch.isnan(o1).any() and not torch.isnan(l1).any()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_dominant_logit_returns_value_row_exactly():
+    """Key j is 64 e_j, query i is 16 e_target(i): one logit per row is
+    16*64/sqrt(128) ~ 90 above all others, whose weights then vanish
+    against it, so each output row is its target's value row, bit for bit."""
+    n = d = 128
+    rng = np.random.default_rng(3)
+    target = rng.permutation(n)
+    q = np.zeros((1, n, 1, d), np.float32)
+    q[0, np.arange(n), 0, target] = 16.0
+    k = np.zeros((1, n, 1, d), np.float32)
+    k[0, np.arange(n), 0, np.arange(n)] = 64.0
+    v = fi.round_to(rng.standard_normal((1, n, 1, d)).astype(np.float32), "bf16")
+    o, _ = fa.fwd(to_dev(fi.round_to(q, "bf16"), "bf16"), to_dev(fi.round_to(k, "bf16"), "bf16"),
+                  to_dev(v, "bf16"), causal=False)
+    og = to_f64(o)[0, :, 0]
+    np.testing.assert_array_equal(og, fi.to_f64(v, "bf16")[0, target, 0])
+
+
+def test_causal_more_queries_than_keys_empty_rows():
+    x = fi.dense(1, 100, 40, 2, 1, 64, "bf16", seed=8, causal=True)
+    o, l = run_dense(x)
+    assert np.all(o[0, :60] == 0) and np.all(l[0, :60] == -np.inf)
+    O, L = oracle.attention(fi.to_f64(x.q, "bf16"), fi.to_f64(x.k, "bf16"), fi.to_f64(x.v, "bf16"),
+                            x.scale, True)
+    assert_parity(o, l, O, L, fi.to_f64(x.v, "bf16"), "bf16", "Nq>Nk causal")
