@@ -68,6 +68,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2)
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, copy this many MiB device-to-device once (a kernel of "
+                         "known traffic, to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
@@ -177,6 +180,15 @@ def main():
                          "frac": gbs / PEAK_HBM_GBS, "traffic": None,
                          "kernel": "decode_split_kernel + decode_combine_kernel"},
         }
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_heads)

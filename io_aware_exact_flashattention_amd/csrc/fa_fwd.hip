@@ -43,6 +43,8 @@ namespace {
 constexpr int kBM = 128;  // query rows per workgroup, 16-bit path
 constexpr int kBN = 64;   // keys per K/V tile, 16-bit path
 constexpr int kThreads = 256;
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maximum.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 struct Work {
   int b, h, tile;
@@ -81,43 +83,62 @@ __device__ __forceinline__ void seq_bounds(const FwdParams& p, int b, int& q0, i
   }
 }
 
-// 16-byte chunk swizzle of an LDS row holding `chunks` chunks: rows that one
-// MFMA operand read touches together map to distinct banks.
-template <int chunks>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (chunks == 16) return row & 15;
-  else return (row >> 1) & 7;
+// LDS geometry of one K or V tile: kBN rows of D 16-bit values, row-major,
+// in 16-byte chunks whose order inside a row is XOR-swizzled by the row.
+template <int D>
+struct TileGeom {
+  static constexpr int ROWB = 2 * D;                    // bytes per row
+  static constexpr int CH = D / 8;                      // chunks per row
+  static constexpr int BYTES = kBN * ROWB;              // bytes per tile
+  static constexpr int LOADS = BYTES / (kThreads * 16); // 16-byte loads per lane per tile
+  // K is read as the A operand of S^T = K Q^T: 32 consecutive rows, one
+  // chunk each; the swizzle spreads any 16 consecutive rows over all banks.
+  __device__ static __forceinline__ int k_swz(int row) {
+    if constexpr (CH == 16) return row & 15;
+    else return (row >> 1) & 7;
+  }
+  // V is read with ds_read_b64_tr_b16: per instruction 8 rows (4 per half
+  // wave) x 64 contiguous bytes; the swizzle moves the 4 rows of a half
+  // wave to disjoint bank groups.
+  __device__ static __forceinline__ int v_swz(int row) {
+    if constexpr (CH == 16) return 4 * (row & 3);
+    else return 4 * ((row >> 1) & 1);
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16. Inside each group of 16 lanes, lane j receives element
+// j%4 of the 8 bytes addressed by lane 4e + j/4, as its element e.
+__device__ __forceinline__ uint2 lds_read_tr(const char* lds_byte_ptr) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_byte_ptr);
+  return __builtin_bit_cast(uint2, v);
 }
 
-// Position of key `key` (0..63 inside a tile) in a V^T row. The score
-// accumulator gives lane-half h, register r of 32-key block kb the key
-// 32kb + 8(r/4) + 4h + r%4; the PV B operand of (kb, u) is registers
-// 8u..8u+7, i.e. keys 16u + {4h..4h+3, 8+4h..8+4h+3}. Those 8 keys sit
-// contiguously at 32kb + 16u + 8h, so one 16-byte LDS read is the matching A
-// operand.
-__device__ __forceinline__ int vt_pos(int key) {
-  const int o = key & 15;
-  return (key & ~15) + 8 * ((o >> 2) & 1) + (o & 3) + 4 * (o >> 3);
-}
-
-__device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+// Direct global -> LDS 16-byte load: lane i of the wave writes LDS bytes
+// [lds_wave_base + 16 i, +16); lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void load_to_lds(const void* gsrc, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                   16, 0, 0);
 }
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams p) {
   using E = Elem<T>;
-  constexpr int KCH = D / 8;    // 16-byte chunks per K row
-  constexpr int VCH = kBN / 8;  // 16-byte chunks per V^T row
+  using G = TileGeom<D>;
   constexpr int KS = D / 16;    // MFMA k-steps of Q K^T
   constexpr int DB = D / 32;    // 32-row blocks of O^T
   constexpr int NB = kBN / 32;  // 32-key blocks per tile
-  constexpr int K_UNITS = kBN * KCH / kThreads;
-  constexpr int V_UNITS = (kBN / 2) * (D / 8) / kThreads;
-  static_assert(K_UNITS >= 1 && V_UNITS >= 1, "tile too small for the workgroup");
+  constexpr int LD = G::LOADS;
 
-  __shared__ uint4 k_lds[2][kBN * KCH];
-  __shared__ uint4 v_lds[2][D * VCH];
+  // Two stages of K and V tiles, as four separate objects: the wait-count
+  // pass can then tell that reads of one stage do not alias the in-flight
+  // direct-to-LDS loads of the other, and does not wait for them.
+  __shared__ __attribute__((aligned(16))) char k_lds0[G::BYTES];
+  __shared__ __attribute__((aligned(16))) char v_lds0[G::BYTES];
+  __shared__ __attribute__((aligned(16))) char k_lds1[G::BYTES];
+  __shared__ __attribute__((aligned(16))) char v_lds1[G::BYTES];
 
   const Work w = map_block(p.n_qtiles, p.Hq);
   int q0, Lq, k0, Lk;
@@ -149,57 +170,69 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = make_uint4(0, 0, 0, 0);
   }
+  // Retire the Q loads on every path before the loop: the wait-count pass
+  // would otherwise treat them as possibly outstanding inside it.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
+  // ---- direct-to-LDS tile loads: this lane's rows and source chunks ----
+  // Load n of thread tid fills LDS bytes (n*kThreads + tid)*16 of a tile;
+  // the swizzle is applied on the source side.
+  int ld_row[LD], k_col[LD], v_col[LD];
+#pragma unroll
+  for (int n = 0; n < LD; ++n) {
+    const int pos = (n * kThreads + tid) * 16;
+    const int r = pos / G::ROWB, pc = (pos % G::ROWB) / 16;
+    ld_row[n] = r;
+    k_col[n] = 8 * (pc ^ G::k_swz(r));
+    v_col[n] = 8 * (pc ^ G::v_swz(r));
+  }
   const uint16_t* kbase = (const uint16_t*)p.k + (int64_t)k0 * p.kv_row + (int64_t)g * D;
   const uint16_t* vbase = (const uint16_t*)p.v + (int64_t)k0 * p.kv_row + (int64_t)g * D;
+  const int last_key = Lk - 1;
 
-  uint4 kreg[K_UNITS];
-  uint4 vreg[V_UNITS][2];
-
-  auto load_tile = [&](int j) {
+  auto issue_tile = [&](int j, char* k_stage, char* v_stage) {
+    char* kl = k_stage + wave * 64 * 16;
+    char* vl = v_stage + wave * 64 * 16;
 #pragma unroll
-    for (int i = 0; i < K_UNITS; ++i) {
-      const int u = tid + kThreads * i;
-      const int r = u / KCH, c = u % KCH;
-      const int key = j * kBN + r;
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      if (key < Lk) kreg[i] = *(const uint4*)(kbase + (int64_t)key * p.kv_row + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < V_UNITS; ++i) {
-      const int u = tid + kThreads * i;
-      const int c = u % (D / 8), m = u / (D / 8);
-      const int key = j * kBN + 2 * m;
-      vreg[i][0] = make_uint4(0, 0, 0, 0);
-      vreg[i][1] = make_uint4(0, 0, 0, 0);
-      if (key < Lk) vreg[i][0] = *(const uint4*)(vbase + (int64_t)key * p.kv_row + c * 8);
-      if (key + 1 < Lk) vreg[i][1] = *(const uint4*)(vbase + (int64_t)(key + 1) * p.kv_row + c * 8);
+    for (int n = 0; n < LD; ++n) {
+      // rows past the sequence end repeat its last row (finite values that
+      // the mask gives weight zero)
+      const int64_t key = min(j * kBN + ld_row[n], last_key);
+      load_to_lds(kbase + key * p.kv_row + k_col[n], kl + n * kThreads * 16);
+      load_to_lds(vbase + key * p.kv_row + v_col[n], vl + n * kThreads * 16);
     }
   };
 
-  auto store_tile = [&](int buf) {
+  // ---- per-lane LDS read offsets (bytes, inside a tile) ----
+  // K, A operand of S^T: row 32kb + l32, logical chunk 2s + hh.
+  int k_off[NB][KS];
 #pragma unroll
-    for (int i = 0; i < K_UNITS; ++i) {
-      const int u = tid + kThreads * i;
-      const int r = u / KCH, c = u % KCH;
-      k_lds[buf][r * KCH + (c ^ swz<KCH>(r))] = kreg[i];
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int r = 32 * kb + l32;
+      k_off[kb][s] = r * G::ROWB + 16 * ((2 * s + hh) ^ G::k_swz(r));
     }
-    uint32_t* vt = (uint32_t*)v_lds[buf];
+  // V, A operand of O^T += V^T P^T via transpose reads. For (kb, u, t) the
+  // 16-lane group reads rows 32kb + 16u + 8t + 4hh + i/4 (i = lane % 16) at
+  // columns d = 32db + 16*((lane/16)%2) + 4*(i%4): lane j of the group then
+  // holds V[those 4 rows][32db + lane%32], which are the keys of its P
+  // fragment (registers 8u + 4t .. +3 of score block kb).
+  const int vi = lane & 15;
+  const int v_gran = 4 * ((lane >> 4) & 1) + (vi & 3);  // 8-byte granule within 32 columns
+  int v_off[NB][2][2][DB];
 #pragma unroll
-    for (int i = 0; i < V_UNITS; ++i) {
-      const int u = tid + kThreads * i;
-      const int c = u % (D / 8), m = u / (D / 8);
-      const int pos = vt_pos(2 * m);  // even; key 2m+1 sits at pos+1
-      const int chunk = pos >> 3, wi = (pos & 7) >> 1;
+  for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a = comp(vreg[i][0], e >> 1), b = comp(vreg[i][1], e >> 1);
-        const uint32_t packed = (e & 1) ? byte_perm(b, a, 0x07060302u) : byte_perm(b, a, 0x05040100u);
-        const int d = 8 * c + e;
-        vt[(d * VCH + (chunk ^ swz<VCH>(d))) * 4 + wi] = packed;
-      }
-    }
-  };
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int r = 32 * kb + 16 * u + 8 * t + 4 * hh + (vi >> 2);
+          const int gran = 8 * db + v_gran;
+          v_off[kb][u][t][db] = r * G::ROWB + 16 * ((gran >> 1) ^ G::v_swz(r)) + 8 * (gran & 1);
+        }
 
   f32x16 acc_o[DB];
 #pragma unroll
@@ -210,100 +243,95 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams p) {
   float l_run = 0.f;        // this lane's share of the running row sum
   const float c2 = p.scale_log2;
 
-  if (n_kv > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < n_kv; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_kv) load_tile(j + 1);
-
+  auto compute_tile = [&](int j, const char* kl, const char* vl) {
     bool active = wrow0 < Lq;
     if (CAUSAL) active = active && (j * kBN <= wrow0 + 31 + delta);
-    if (active) {
-      // ---- partial scores S^T = K_j Q^T (two 32x32 blocks) ----
-      f32x16 acc_s[NB];
+    if (!active) return;
+    // ---- partial scores S^T = K_j Q^T ----
+    f32x16 acc_s[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_s[kb][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_s[kb][r] = 0.f;
-        const int krow = 32 * kb + l32;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const uint4 a = k_lds[buf][krow * KCH + ((2 * s + hh) ^ swz<KCH>(krow))];
-          acc_s[kb] = E::mma32(a, qf[s], acc_s[kb]);
-        }
+        const uint4 a = *(const uint4*)(kl + k_off[kb][s]);
+        acc_s[kb] = E::mma32(a, qf[s], acc_s[kb]);
       }
-      // ---- mask keys past the sequence end / above the diagonal ----
-      const bool need_mask =
-          (j * kBN + kBN > Lk) || (CAUSAL && (j * kBN + kBN - 1 > wrow0 + delta));
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j * kBN + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            bool vis = key < Lk;
-            if (CAUSAL) vis = vis && (key <= my_row + delta);
-            if (!vis) acc_s[kb][r] = neg_inf();
-          }
-      }
-      // ---- online softmax: running max m, running sum l ----
-      float mx = neg_inf();
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[kb][r]);
-      mx = fmaxf(mx, xor_lane(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c2);
-      const float base = (m_new == neg_inf()) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - base);
-      float rs = 0.f;
+    // ---- mask keys past the sequence end / above the diagonal ----
+    const bool need_mask = (j * kBN + kBN > Lk) || (CAUSAL && (j * kBN + kBN - 1 > wrow0 + delta));
+    if (need_mask) {
+      const int lim = CAUSAL ? min(Lk - 1, my_row + delta) : Lk - 1;
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(acc_s[kb][r], c2, -base));
-          acc_s[kb][r] = e;
-          rs += e;
+          const int key = j * kBN + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key > lim) acc_s[kb][r] = neg_inf();
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-      }
-      // ---- O^T += V_j^T P^T ----
-      uint4 pf[NB][2];
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 8 * u;
-          pf[kb][u] = make_uint4(E::pack2(acc_s[kb][r + 0], acc_s[kb][r + 1]),
-                                 E::pack2(acc_s[kb][r + 2], acc_s[kb][r + 3]),
-                                 E::pack2(acc_s[kb][r + 4], acc_s[kb][r + 5]),
-                                 E::pack2(acc_s[kb][r + 6], acc_s[kb][r + 7]));
-        }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = 32 * db + l32;
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int chunk = 4 * kb + 2 * u + hh;
-            const uint4 a = v_lds[buf][d * VCH + (chunk ^ swz<VCH>(d))];
-            acc_o[db] = E::mma32(a, pf[kb][u], acc_o[db]);
-          }
-      }
     }
+    // ---- online softmax: running max m, running sum l ----
+    float mx = neg_inf();
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[kb][r]);
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    const float m_new = fmaxf(m_run, mx * c2);
+    const float base = (m_new == neg_inf()) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - base);
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(acc_s[kb][r], c2, -base));
+        acc_s[kb][r] = e;
+        rs += e;
+      }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+    }
+    // ---- O^T += V_j^T P^T ----
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = 8 * u;
+        const uint4 pf = make_uint4(E::pack2(acc_s[kb][r + 0], acc_s[kb][r + 1]),
+                                    E::pack2(acc_s[kb][r + 2], acc_s[kb][r + 3]),
+                                    E::pack2(acc_s[kb][r + 4], acc_s[kb][r + 5]),
+                                    E::pack2(acc_s[kb][r + 6], acc_s[kb][r + 7]));
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint2 lo = lds_read_tr(vl + v_off[kb][u][0][db]);
+          const uint2 hi = lds_read_tr(vl + v_off[kb][u][1][db]);
+          acc_o[db] = E::mma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pf, acc_o[db]);
+        }
+      }
+  };
 
-    if (j + 1 < n_kv) store_tile(buf ^ 1);
+  if (n_kv > 0) issue_tile(0, k_lds0, v_lds0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+
+  // Two tiles per trip so that each LDS stage is addressed statically.
+  for (int j = 0; j < n_kv; j += 2) {
+    if (j + 1 < n_kv) issue_tile(j + 1, k_lds1, v_lds1);
+    compute_tile(j, k_lds0, v_lds0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (j + 1 >= n_kv) break;
+    if (j + 2 < n_kv) issue_tile(j + 2, k_lds0, v_lds0);
+    compute_tile(j + 1, k_lds1, v_lds1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
 

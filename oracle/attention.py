@@ -36,11 +36,18 @@ import numpy as np
 ROW_BLOCK = 2048
 
 
+def _values(a):
+    """float64 view of values. Integer arrays are refused: 16-bit storage
+    (e.g. bfloat16 bit patterns) must be decoded by the caller first."""
+    a = np.asarray(a)
+    if not np.issubdtype(a.dtype, np.floating):
+        raise TypeError(f"oracle inputs must be floating point values, got {a.dtype}")
+    return a.astype(np.float64, copy=False)
+
+
 def attention_head(q, k, v, scale, causal):
     """One head. q [Nq, d], k [Nk, d], v [Nk, dv] (float64) -> (O [Nq, dv], lse [Nq])."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+    q, k, v = _values(q), _values(k), _values(v)
     Nq, Nk = q.shape[0], k.shape[0]
     return attention_rows(q, np.arange(Nq), Nq, k, v, scale, causal)
 
@@ -56,9 +63,7 @@ def attention_rows(q_rows, rows, Nq, k, v, scale, causal):
     k x k score matrix": S = Q K^T for the rows, a softmax over each complete
     row (max, exponentials, sum), then the weighted sum of the value rows.
     """
-    q_rows = np.asarray(q_rows, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+    q_rows, k, v = _values(q_rows), _values(k), _values(v)
     rows = np.asarray(rows, dtype=np.int64)
     R, Nk, dv = q_rows.shape[0], k.shape[0], v.shape[1]
     O = np.zeros((R, dv), dtype=np.float64)
@@ -94,9 +99,7 @@ def attention(q, k, v, scale, causal):
     Multi-head and grouped-query attention as listed in "I/O-Aware Kernels",
     section "FlashInfer: I/O-aware attention for serving": each query head is
     an independent instance of the definition on its key/value head."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+    q, k, v = _values(q), _values(k), _values(v)
     B, Nq, Hq, _ = q.shape
     Hkv = k.shape[2]
     if Hq % Hkv:
@@ -117,9 +120,7 @@ def attention_varlen(q, k, v, cu_q, cu_k, scale, causal):
     is applied to each sequence on its own ("I/O-Aware Kernels", section
     "FlashInfer: I/O-aware attention for serving": ragged, variable-length
     batches)."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+    q, k, v = _values(q), _values(k), _values(v)
     Hq, Hkv = q.shape[1], k.shape[1]
     O = np.zeros(q.shape[:2] + (v.shape[2],), dtype=np.float64)
     lse = np.zeros(q.shape[:2], dtype=np.float64)
@@ -143,15 +144,15 @@ def decode(q, k_seq, v_seq, cu_k, scale, seqs=None):
     attention for serving", only changes where K/V live, not the result.
     Returns O [B, Hq, d], lse [B, Hq].
     """
-    q = np.asarray(q, dtype=np.float64)
+    q = _values(q)
     B, Hq, _ = q.shape
     Hkv = k_seq.shape[1]
     O = np.zeros(q.shape[:2] + (v_seq.shape[2],), dtype=np.float64)
     lse = np.full((B, Hq), -np.inf, dtype=np.float64)
     for b in (range(B) if seqs is None else seqs):
         k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
-        kb = np.asarray(k_seq[k0:k1], dtype=np.float64)
-        vb = np.asarray(v_seq[k0:k1], dtype=np.float64)
+        kb = _values(k_seq[k0:k1])
+        vb = _values(v_seq[k0:k1])
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             o, l = attention_head(q[b, h][None, :], kb[:, g], vb[:, g], scale, causal=False)

@@ -26,17 +26,26 @@ def run(x: fi.Paged, num_splits=0, dev=None):
     return o, l
 
 
+def oracle_for(x: fi.Paged, seqs):
+    """fp64 oracle of the sampled sequences, fed their contiguous K/V."""
+    k = [fi.to_f64(x.k_seq[x.cu_k[b]:x.cu_k[b + 1]], x.dtype) for b in seqs]
+    v = [fi.to_f64(x.v_seq[x.cu_k[b]:x.cu_k[b + 1]], x.dtype) for b in seqs]
+    cu = np.concatenate([[0], np.cumsum([len(a) for a in k])]).astype(np.int64)
+    shape = (0,) + x.k_seq.shape[1:]
+    k = np.concatenate(k) if k else np.zeros(shape)
+    v = np.concatenate(v) if v else np.zeros(shape)
+    O, L = oracle.decode(fi.to_f64(x.q[seqs], x.dtype), k, v, cu, x.scale)
+    return O, L, v
+
+
 def check(x: fi.Paged, what, seqs=None, num_splits=0, dev=None):
     print(f"[case] {what} B={len(x.seq_lens)} splits={num_splits}", flush=True)
     o, l = run(x, num_splits, dev)
     o, l = to_f64(o), to_f64(l)
-    seqs = list(range(len(x.seq_lens))) if seqs is None else seqs
-    O, L = oracle.decode(fi.to_f64(x.q, x.dtype), x.k_seq, x.v_seq, x.cu_k, x.scale, seqs=seqs)
-    O = np.stack([O[b] for b in seqs])
-    L = np.stack([L[b] for b in seqs])
-    v_read = np.concatenate([fi.to_f64(x.v_seq[x.cu_k[b]:x.cu_k[b + 1]], x.dtype).ravel()
-                             for b in seqs] + [np.zeros(1)])
-    return assert_parity(o[seqs], l[seqs], O, L, v_read, x.dtype, what)
+    seqs = list(range(len(x.seq_lens))) if seqs is None else list(seqs)
+    O, L, v_read = oracle_for(x, seqs)
+    return assert_parity(o[seqs], l[seqs], O, L, np.concatenate([v_read.ravel(), [0.0]]),
+                         x.dtype, what)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])

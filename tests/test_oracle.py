@@ -80,3 +80,10 @@ def test_rows_subset_equals_whole():
     o, l = oracle.attention_rows(q[rows], rows, 50, k, v, 0.3, True)
     np.testing.assert_array_equal(o, O[rows])
     np.testing.assert_array_equal(l, L[rows])
+
+
+def test_oracle_refuses_integer_storage():
+    """16-bit storage must be decoded to values before reaching the oracle."""
+    bits = np.zeros((4, 8), dtype=np.uint16)
+    with pytest.raises(TypeError):
+        oracle.attention_head(bits, bits, bits, 0.5, False)
