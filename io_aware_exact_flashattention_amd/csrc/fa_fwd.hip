@@ -40,11 +40,17 @@
 namespace fa {
 namespace {
 
-constexpr int kBM = 128;  // query rows per workgroup, 16-bit path
-constexpr int kBN = 64;   // keys per K/V tile, 16-bit path
-constexpr int kThreads = 256;
+constexpr int kBM = 256;      // query rows per workgroup, 16-bit path (8 waves x 32)
+constexpr int kBN = 64;       // keys per K/V tile, 16-bit path
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kStages = 4;    // LDS ring of K/V tiles
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maximum.
 constexpr int kWaitVmcnt0 = 0x0F70;
+// s_waitcnt immediate: vmcnt(n) for n < 16, expcnt and lgkmcnt at their maximum.
+constexpr int wait_vmcnt(int n) { return 0x0F70 | n; }
+// Rescale threshold of the running max (log2 units): weights stay <= 2^8.
+constexpr float kRescale = 8.f;
 
 struct Work {
   int b, h, tile;
@@ -116,29 +122,45 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* lds_byte_ptr) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// Direct global -> LDS 16-byte load: lane i of the wave writes LDS bytes
-// [lds_wave_base + 16 i, +16); lds_wave_base must be wave-uniform.
-__device__ __forceinline__ void load_to_lds(const void* gsrc, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base,
-                                   16, 0, 0);
+// Direct global -> LDS 16-byte load (global_load_lds_dwordx4): lane i of
+// the wave writes LDS bytes [lds_wave_base + 16 i, +16); lds_wave_base is a
+// wave-uniform LDS byte address (goes to M0). Written as inline assembly so
+// that the compiler's wait-count pass does not treat every later LDS read as
+// possibly aliasing it; completion is awaited explicitly with s_waitcnt
+// vmcnt before the workgroup barrier that publishes the tile.
+__device__ __forceinline__ void load_to_lds(const void* gsrc, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(lds_wave_base)
+               : "memory", "m0");
+}
+
+// Keep a value's computation ahead of this point: the empty volatile asm
+// "uses" it, and the compiler does not move volatile asm across the
+// scheduling fences that lay out the MFMA/softmax overlap.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint4& x) {
+  asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   using E = Elem<T>;
   using G = TileGeom<D>;
   constexpr int KS = D / 16;    // MFMA k-steps of Q K^T
   constexpr int DB = D / 32;    // 32-row blocks of O^T
   constexpr int NB = kBN / 32;  // 32-key blocks per tile
   constexpr int LD = G::LOADS;
+  constexpr int TILE_LOADS = 2 * LD;             // K and V loads per lane per tile
+  constexpr int STAGE = 2 * G::BYTES;            // one K tile then one V tile
 
-  // Two stages of K and V tiles, as four separate objects: the wait-count
-  // pass can then tell that reads of one stage do not alias the in-flight
-  // direct-to-LDS loads of the other, and does not wait for them.
-  __shared__ __attribute__((aligned(16))) char k_lds0[G::BYTES];
-  __shared__ __attribute__((aligned(16))) char v_lds0[G::BYTES];
-  __shared__ __attribute__((aligned(16))) char k_lds1[G::BYTES];
-  __shared__ __attribute__((aligned(16))) char v_lds1[G::BYTES];
+  // Ring of kStages (K, V) tile pairs. Tile j lives in stage j % kStages; it
+  // is loaded two steps before its keys are first used.
+  __shared__ __attribute__((aligned(16))) char lds[kStages * STAGE];
 
   const Work w = map_block(p.n_qtiles, p.Hq);
   int q0, Lq, k0, Lk;
@@ -147,7 +169,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams p) {
   if (row0 >= Lq) return;  // ragged batch: this sequence has fewer tiles
 
   const int g = w.h / p.group;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int delta = Lk - Lq;  // bottom-right causal offset
 
@@ -170,8 +193,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = make_uint4(0, 0, 0, 0);
   }
-  // Retire the Q loads on every path before the loop: the wait-count pass
-  // would otherwise treat them as possibly outstanding inside it.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // ---- direct-to-LDS tile loads: this lane's rows and source chunks ----
@@ -189,77 +210,100 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams p) {
   const uint16_t* kbase = (const uint16_t*)p.k + (int64_t)k0 * p.kv_row + (int64_t)g * D;
   const uint16_t* vbase = (const uint16_t*)p.v + (int64_t)k0 * p.kv_row + (int64_t)g * D;
   const int last_key = Lk - 1;
+  const uint32_t lds0 = lds_address(lds);
+  const uint32_t lds_wave = lds0 + wave * 64 * 16;
 
-  auto issue_tile = [&](int j, char* k_stage, char* v_stage) {
-    char* kl = k_stage + wave * 64 * 16;
-    char* vl = v_stage + wave * 64 * 16;
+  auto issue_tile = [&](int j) {
+    const uint32_t st = lds_wave + (j % kStages) * STAGE;
 #pragma unroll
     for (int n = 0; n < LD; ++n) {
       // rows past the sequence end repeat its last row (finite values that
       // the mask gives weight zero)
       const int64_t key = min(j * kBN + ld_row[n], last_key);
-      load_to_lds(kbase + key * p.kv_row + k_col[n], kl + n * kThreads * 16);
-      load_to_lds(vbase + key * p.kv_row + v_col[n], vl + n * kThreads * 16);
+      load_to_lds(kbase + key * p.kv_row + k_col[n], st + n * kThreads * 16);
+      load_to_lds(vbase + key * p.kv_row + v_col[n], st + G::BYTES + n * kThreads * 16);
     }
   };
 
   // ---- per-lane LDS read offsets (bytes, inside a tile) ----
-  // K, A operand of S^T: row 32kb + l32, logical chunk 2s + hh.
-  int k_off[NB][KS];
+  // K, A operand of S^T: row 32kb + l32, logical chunk 2s + hh. The kb term
+  // (32 rows) leaves the swizzle unchanged and is an immediate offset.
+  int k_off[KS];
 #pragma unroll
-  for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int r = 32 * kb + l32;
-      k_off[kb][s] = r * G::ROWB + 16 * ((2 * s + hh) ^ G::k_swz(r));
-    }
+  for (int s = 0; s < KS; ++s) k_off[s] = l32 * G::ROWB + 16 * ((2 * s + hh) ^ G::k_swz(l32));
   // V, A operand of O^T += V^T P^T via transpose reads. For (kb, u, t) the
   // 16-lane group reads rows 32kb + 16u + 8t + 4hh + i/4 (i = lane % 16) at
   // columns d = 32db + 16*((lane/16)%2) + 4*(i%4): lane j of the group then
   // holds V[those 4 rows][32db + lane%32], which are the keys of its P
-  // fragment (registers 8u + 4t .. +3 of score block kb).
+  // fragment (registers 8u + 4t .. +3 of score block kb). Multiples of 8
+  // rows leave the swizzle unchanged and are immediate offsets.
   const int vi = lane & 15;
-  const int v_gran = 4 * ((lane >> 4) & 1) + (vi & 3);  // 8-byte granule within 32 columns
-  int v_off[NB][2][2][DB];
+  const int v_row = 4 * hh + (vi >> 2);
+  int v_off[DB];
 #pragma unroll
-  for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int r = 32 * kb + 16 * u + 8 * t + 4 * hh + (vi >> 2);
-          const int gran = 8 * db + v_gran;
-          v_off[kb][u][t][db] = r * G::ROWB + 16 * ((gran >> 1) ^ G::v_swz(r)) + 8 * (gran & 1);
-        }
+  for (int db = 0; db < DB; ++db) {
+    const int gran = 8 * db + 4 * ((lane >> 4) & 1) + (vi & 3);  // 8-byte granule of the row
+    v_off[db] = G::BYTES + v_row * G::ROWB + 16 * ((gran >> 1) ^ G::v_swz(v_row)) + 8 * (gran & 1);
+  }
 
   f32x16 acc_o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
-  float m_run = neg_inf();  // running max of scaled logits, log2 domain
+  // Reference max of the scaled logits (log2 domain). It is raised only
+  // when a tile brings a logit more than kRescale above it, so the weights
+  // exp2(s - m_ref) stay below 2^kRescale and most tiles skip the O rescale;
+  // numerator and denominator share the reference, so the result is the
+  // same as with the exact running max.
+  float m_run = neg_inf();
   float l_run = 0.f;        // this lane's share of the running row sum
   const float c2 = p.scale_log2;
 
-  auto compute_tile = [&](int j, const char* kl, const char* vl) {
-    bool active = wrow0 < Lq;
-    if (CAUSAL) active = active && (j * kBN <= wrow0 + 31 + delta);
-    if (!active) return;
-    // ---- partial scores S^T = K_j Q^T ----
-    f32x16 acc_s[NB];
+  // scores of tile j (s_cur) and of tile j+1 (s_nxt)
+  f32x16 s_cur[NB], s_nxt[NB];
+  auto scores = [&](const char* stage, f32x16* acc) {
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc_s[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s) {
+      const char* kp = stage + k_off[s];
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
-        const uint4 a = *(const uint4*)(kl + k_off[kb][s]);
-        acc_s[kb] = E::mma32(a, qf[s], acc_s[kb]);
+        const uint4 a = *(const uint4*)(kp + kb * 32 * G::ROWB);
+        acc[kb] = E::mma32(a, qf[s], acc[kb]);
       }
+      // bound the K fragments held in registers (two k-steps in flight)
+      if (s % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- prologue: tiles 0..2 in flight, scores of tile 0 ----
+  for (int j = 0; j < min(n_kv, kStages - 1); ++j) issue_tile(j);
+  if (n_kv > 2) __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * TILE_LOADS));
+  else if (n_kv > 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(TILE_LOADS));
+  else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (n_kv > 0) scores(lds, s_cur);
+
+  // One pipeline step: the softmax and P.V of tile j, plus the scores of
+  // tile j+1. The score MFMAs of tile j+1 and the softmax of tile j are
+  // independent; they are laid out as KS chunks, each "read the next K
+  // fragments, two MFMAs, a slice of the softmax", fenced so the compiler
+  // keeps that order: the matrix core works on the MFMAs while the vector
+  // ALUs work on the softmax slice.
+  auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt) {
+    const char* st_cur = lds + (j % kStages) * STAGE;
+    const char* st_nxt = lds + ((j + 1) % kStages) * STAGE;
+    // tile j+1 has landed for every wave, and every wave is done with the
+    // stage that tile j+3 goes to (it held tile j-1)
+    if (j + 2 < n_kv) __builtin_amdgcn_s_waitcnt(wait_vmcnt(TILE_LOADS));
+    else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (j + 3 < n_kv) issue_tile(j + 3);
+
     // ---- mask keys past the sequence end / above the diagonal ----
     const bool need_mask = (j * kBN + kBN > Lk) || (CAUSAL && (j * kBN + kBN - 1 > wrow0 + delta));
     if (need_mask) {
@@ -269,70 +313,95 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j * kBN + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key > lim) acc_s[kb][r] = neg_inf();
+          if (key > lim) s_cur[kb][r] = neg_inf();
         }
     }
-    // ---- online softmax: running max m, running sum l ----
-    float mx = neg_inf();
+
+    // ---- S_{j+1} = K_{j+1} Q^T  ||  online softmax of tile j ----
+    // (past the last tile the next stage holds stale data; those scores are
+    // never used)
+    constexpr int MAXC = KS / 2;       // chunks that reduce the row max
+    constexpr int EXPC = KS - MAXC;    // chunks that exponentiate
+    constexpr int GROUPS = 2 * NB;     // groups of 8 probabilities
+    constexpr int PER_MAX = 16 * NB / MAXC;
+    constexpr int PER_EXP = GROUPS / EXPC;
+    static_assert(PER_EXP >= 1 && GROUPS % EXPC == 0 && (16 * NB) % MAXC == 0, "chunking");
+    uint4 kfr[2][NB];
+    uint4 pf[NB][2];
+    float mx = neg_inf(), rs = 0.f, alpha = 1.f, base = 0.f;
+    bool raise = false;
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
+    for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[kb][r]);
-    mx = fmaxf(mx, xor_lane(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float base = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - base);
-    float rs = 0.f;
+      for (int r = 0; r < 16; ++r) s_nxt[kb][r] = 0.f;
+      kfr[0][kb] = *(const uint4*)(st_nxt + k_off[0] + kb * 32 * G::ROWB);
+    }
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(acc_s[kb][r], c2, -base));
-        acc_s[kb][r] = e;
-        rs += e;
+        for (int kb = 0; kb < NB; ++kb)
+          kfr[(s + 1) & 1][kb] = *(const uint4*)(st_nxt + k_off[s + 1] + kb * 32 * G::ROWB);
       }
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) s_nxt[kb] = E::mma32(kfr[s & 1][kb], qf[s], s_nxt[kb]);
+      if (s < MAXC) {
+#pragma unroll
+        for (int i = s * PER_MAX; i < (s + 1) * PER_MAX; ++i) mx = fmaxf(mx, s_cur[i / 16][i % 16]);
+        if (s == MAXC - 1) mx = fmaxf(mx, xor_lane(mx, 32));
+        pin(mx);
+      } else {
+        if (s == MAXC) {
+          const float mx2 = mx * c2;  // -inf when the row sees no key of this tile
+          raise = mx2 > m_run + kRescale;
+          alpha = fast_exp2(raise ? m_run - mx2 : 0.f);  // exp2(0) = 1
+          m_run = raise ? mx2 : m_run;
+          base = (m_run == neg_inf()) ? 0.f : m_run;
+        }
+#pragma unroll
+        for (int gi = (s - MAXC) * PER_EXP; gi < (s - MAXC + 1) * PER_EXP; ++gi) {
+          const int kb = gi / 2, u = gi % 2;
+          float e[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            e[i] = fast_exp2(fmaf(s_cur[kb][8 * u + i], c2, -base));
+            rs += e[i];
+          }
+          pf[kb][u] = make_uint4(E::pack2(e[0], e[1]), E::pack2(e[2], e[3]),
+                                 E::pack2(e[4], e[5]), E::pack2(e[6], e[7]));
+          pin(pf[kb][u]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     l_run = l_run * alpha + rs;
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {
+    if (__ballot(raise)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
     }
-    // ---- O^T += V_j^T P^T ----
+
+    // ---- O^T += V_j^T P_j^T ----
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
+    for (int db = 0; db < DB; ++db) {
+      const char* vp = st_cur + v_off[db];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r = 8 * u;
-        const uint4 pf = make_uint4(E::pack2(acc_s[kb][r + 0], acc_s[kb][r + 1]),
-                                    E::pack2(acc_s[kb][r + 2], acc_s[kb][r + 3]),
-                                    E::pack2(acc_s[kb][r + 4], acc_s[kb][r + 5]),
-                                    E::pack2(acc_s[kb][r + 6], acc_s[kb][r + 7]));
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint2 lo = lds_read_tr(vl + v_off[kb][u][0][db]);
-          const uint2 hi = lds_read_tr(vl + v_off[kb][u][1][db]);
-          acc_o[db] = E::mma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pf, acc_o[db]);
+        for (int u = 0; u < 2; ++u) {
+          const char* vq = vp + (32 * kb + 16 * u) * G::ROWB;
+          const uint2 lo = lds_read_tr(vq);
+          const uint2 hi = lds_read_tr(vq + 8 * G::ROWB);
+          acc_o[db] = E::mma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pf[kb][u], acc_o[db]);
         }
-      }
+    }
   };
 
-  if (n_kv > 0) issue_tile(0, k_lds0, v_lds0);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-
-  // Two tiles per trip so that each LDS stage is addressed statically.
-  for (int j = 0; j < n_kv; j += 2) {
-    if (j + 1 < n_kv) issue_tile(j + 1, k_lds1, v_lds1);
-    compute_tile(j, k_lds0, v_lds0);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (j + 1 >= n_kv) break;
-    if (j + 2 < n_kv) issue_tile(j + 2, k_lds0, v_lds0);
-    compute_tile(j + 1, k_lds1, v_lds1);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
+  for (int j = 0; j < n_kv; ++j) {
+    step(j, s_cur, s_nxt);
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) s_cur[kb] = s_nxt[kb];
   }
 
   // ---- epilogue: O = O / l, LSE = ln(sum exp) ----
