@@ -113,7 +113,9 @@ size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_pages, int p
  *   seq_lens   device int32 [B], 0 <= seq_lens[b] <= max_pages*page_size
  *   o [B, Hq, d] dtype, lse [B, Hq] float32 (written)
  *   num_splits 0 = automatic (32 pages per split), else the number of key
- *              splits of the longest sequence (1 .. max_pages)
+ *              splits of the longest sequence (1 .. max_pages); a split never
+ *              holds more than 64 pages, so smaller values are raised to
+ *              ceil(max_pages / 64)
  *   workspace  device buffer of at least
  *              fa_decode_paged_workspace_size(B, Hq, d, max_pages, page_size,
  *              num_splits) bytes, owned by the caller; its contents are

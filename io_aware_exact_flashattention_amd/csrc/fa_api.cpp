@@ -13,6 +13,7 @@ namespace {
 
 constexpr int kPageSize = 16;
 constexpr int kAutoPagesPerSplit = 32;
+constexpr int kMaxPagesPerSplit = 64;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -102,9 +103,13 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   return run_fwd(p, dtype, d, causal, max_seqlen_q, stream);
 }
 
+// Pages per split: 32 when automatic; otherwise the longest sequence is cut
+// into num_splits ranges, but a range never exceeds kMaxPagesPerSplit pages
+// (the decode kernel holds one split's page indices in the lanes of a wave).
 static int pages_per_split(int max_pages, int num_splits) {
   if (num_splits <= 0) return kAutoPagesPerSplit;
-  return (max_pages + num_splits - 1) / num_splits;
+  const int pps = (max_pages + num_splits - 1) / num_splits;
+  return pps < kMaxPagesPerSplit ? pps : kMaxPagesPerSplit;
 }
 
 size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_pages, int page_size,
@@ -134,8 +139,8 @@ fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
   if (need == 0 || workspace_bytes < need) return FA_ERR_INVALID_ARG;
   const int pps = pages_per_split(max_pages, num_splits);
   const int splits = (max_pages + pps - 1) / pps;
-  if ((int64_t)splits > 65535 * 16 || (int64_t)Hkv * Hq > 65535 || B > 65535)
-    return FA_ERR_UNSUPPORTED;
+  if (B > 65535) return FA_ERR_UNSUPPORTED;  // grid y of the split merge
+  if ((int64_t)B * splits * Hq > INT32_MAX) return FA_ERR_UNSUPPORTED;  // work items
 
   fa::DecodeParams p{};
   p.q = q; p.k_pool = k_pool; p.v_pool = v_pool; p.o = o; p.lse = lse;

@@ -40,6 +40,13 @@ namespace {
 constexpr int kPage = 16;
 constexpr float kRescaleThreshold = 8.f;  // log2 units
 
+// Chunk permutation of K row t in a staging slot (VCH 16-byte chunks per
+// row): 16 consecutive rows read at one logical chunk land on 16 distinct
+// 16-byte bank groups.
+template <int VCH> __device__ __forceinline__ int kswz(int t) {
+  return VCH == 16 ? (t & 15) : ((t >> 1) & 7);
+}
+
 template <typename T> struct Mma16;
 template <> struct Mma16<Bf16> {
   // D(16x16, f32) += A(16x32) * B(32x16); 8 bf16 per lane per operand.
@@ -55,49 +62,90 @@ template <> struct Mma16<F16> {
   }
 };
 
-__device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
 __device__ __forceinline__ float lane_value(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
-// One wavefront per (sequence b, KV head g, head block, split s).
+constexpr int kWavesPerBlock = 4;
+constexpr int kWaveLds = 8192;  // LDS bytes per wave: the staging ring of its pages
+
+// Waits written as inline assembly with a memory clobber, so that the LDS
+// reads of a page stay after the wait for its direct-to-LDS loads, and the
+// next loads into a slot stay after the reads that empty it.
+template <int N> __device__ __forceinline__ void wait_loads() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds_reads() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+// Make the compiler consider a loaded value complete here (its own wait
+// count for the load is then settled before the direct-to-LDS loads start).
+__device__ __forceinline__ void settle(uint4& x) {
+  asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+}
+__device__ __forceinline__ void settle(int& x) { asm volatile("" : "+v"(x)); }
+
+// One wavefront per work item (sequence b, KV head g, block of GB query
+// heads, split s); four independent wavefronts per workgroup.
+//
+// Each page of a split is copied by direct-to-LDS loads (no registers held
+// while in flight) into the wave's 8 KB staging ring: one page slot for
+// d = 128, two for d = 64. The next page's loads are issued as soon as the
+// current page has been read out of its slot, so a page is in flight during
+// the whole computation of the previous one.
 //
 // Scores of a 16-token page for the GB query heads of the block come from
 // v_mfma_f32_16x16x32: A = the page's K rows (lane l: token l%16, an 8-value
 // slice of d chosen by l/16), B = Q^T (lane l: query head l%16, zero past
 // GB). In the 16x16 result lane l holds tokens 4(l/16)+i of head l%16.
-// The running max of each head is wave-uniform (kept in scalar registers):
-// a page max is reduced over the token lanes and read back with readlane.
-// The probabilities go through a small LDS array to the P.V lanes, where
-// lane (tg, c) owns the 16-byte slice c of d for tokens tg, tg+TPI, ... and
-// accumulates O on the vector ALUs (V is read in its natural row layout).
-template <typename T, int D, int GB>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
-  using E = Elem<T>;
-  constexpr int KSTEP = D / 32;  // MFMA k-steps per page
-  constexpr int DL = D / 4;      // d values per lane group in the score MFMA
-  constexpr int VCH = D / 8;     // 16-byte chunks per V row
-  constexpr int TPI = 64 / VCH;  // tokens covered by one V load instruction
-  constexpr int VI = kPage / TPI;
-  static_assert(GB <= 16 && VI >= 1, "bad decode tile");
-  __shared__ float p_lds[2][kPage * GB];
+// The running max of each head is wave-uniform: a page max is reduced over
+// the token lanes and read back with readlane.
+// P.V on the vector ALUs: lane c owns d values c*VPL .. c*VPL+VPL-1 (VPL =
+// d/64) of every head of the block for all 16 tokens, so each probability
+// is a wave-wide scalar (readlane) and no lane exchange is needed at the end.
+// Five waves per SIMD (five workgroups per CU) is what the LDS rings allow;
+// the widest head block needs more registers and runs four.
+template <int D, int GB> constexpr int decode_waves_per_simd() { return D * GB > 512 ? 4 : 5; }
 
-  const int s = blockIdx.x, b = blockIdx.z;
+template <typename T, int D, int GB>
+__global__ __launch_bounds__(64 * kWavesPerBlock)
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode_split_kernel(
+    DecodeParams p) {
+  using E = Elem<T>;
+  constexpr int KSTEP = D / 32;       // MFMA k-steps per page (K loads per page)
+  constexpr int DL = D / 4;           // d values per lane group in the score MFMA
+  constexpr int VCH = D / 8;          // 16-byte chunks per token row
+  constexpr int TPI = 64 / VCH;       // tokens per V load instruction
+  constexpr int VI = kPage / TPI;     // V loads per page
+  constexpr int NLOAD = KSTEP + VI;   // direct-to-LDS loads per page
+  constexpr int KBYTES = kPage * D * 2;
+  constexpr int SLOT = 2 * KBYTES;
+  constexpr int NSLOT = kWaveLds / SLOT;
+  constexpr int VPL = D / 64;         // d values per lane in P.V
+  static_assert(GB <= 16 && VI >= 1 && (NSLOT == 1 || NSLOT == 2), "bad decode tile");
+  static_assert(KSTEP * 1024 == KBYTES && VI * 1024 == KBYTES, "page layout");
+  __shared__ uint4 lds[kWavesPerBlock][kWaveLds / 16];
+
+  // work item: (sequence, split, KV head, head block), head block fastest
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int nhb = p.group / GB;
-  const int g = blockIdx.y / nhb;
-  const int h0 = g * p.group + (blockIdx.y % nhb) * GB;
+  const int nh = p.Hkv * nhb;
+  int item = blockIdx.x * kWavesPerBlock + wave;
+  const int hb = item % nh;
+  item /= nh;
+  const int s = item % p.max_splits;
+  const int b = item / p.max_splits;
+  if (b >= p.B) return;
+  const int g = hb / nhb;
+  const int h0 = g * p.group + (hb % nhb) * GB;
   const int L = p.seq_lens[b];
   const int npages = (L + kPage - 1) / kPage;
   const int pg0 = s * p.pages_per_split;
   if (pg0 >= npages) return;
   const int pg1 = min(npages, pg0 + p.pages_per_split);
 
-  const int lane = threadIdx.x;
-  const int l16 = lane & 15, j = lane >> 4;   // score layout
-  const int c = lane % VCH, tg = lane / VCH;  // P.V layout
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, j = lane >> 4;  // score layout
   const float c2 = p.scale_log2;
 
   // B operand: Q^T, heads h0 .. h0+GB-1 in columns 0..GB-1
@@ -109,40 +157,85 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int st = 0; st < KSTEP; ++st) qf[st] = *(const uint4*)(src + 8 * st);
   }
+  // Page indices of the split (at most 64 pages): lane i holds entry
+  // pg0 + i; each page's index is read from its lane.
+  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
+  int pg_idx = pg0 + lane < pg1 ? pt[pg0 + lane] : 0;
+#pragma unroll
+  for (int st = 0; st < KSTEP; ++st) settle(qf[st]);
+  settle(pg_idx);
+
+  // Direct-to-LDS copies of whole token rows (each load instruction reads
+  // TPI complete rows, so every cache line is requested once). In the
+  // slot, K and V are row-major [token][d]; the 16-byte chunks of K row t
+  // are stored XOR-permuted by kswz(t) so that the score operand reads
+  // (16 tokens, one chunk each) hit distinct LDS banks.
+  const int64_t tok = (int64_t)p.Hkv * D;  // elements between tokens of a page
+  const int dma_t = lane / VCH, dma_c = lane % VCH;  // row and stored chunk of this lane
+  const uint16_t* kdma = (const uint16_t*)p.k_pool + (int64_t)g * D + dma_t * tok;
+  const uint16_t* vdma = (const uint16_t*)p.v_pool + (int64_t)g * D + dma_c * 8 + dma_t * tok;
+  int kcol[KSTEP];  // K chunk fetched by this lane for load st (un-permuted)
+#pragma unroll
+  for (int st = 0; st < KSTEP; ++st) kcol[st] = 8 * (dma_c ^ kswz<VCH>(st * TPI + dma_t));
+  const uint32_t ring = lds_address(&lds[wave][0]);
+  const char* ring_ptr = (const char*)&lds[wave][0];
+  auto issue_page = [&](int pg, int slot) {
+    const int64_t base = (int64_t)__builtin_amdgcn_readlane(pg_idx, pg - pg0) * kPage * tok;
+    const uint32_t dst = ring + slot * SLOT;
+#pragma unroll
+    for (int st = 0; st < KSTEP; ++st)
+      stream_to_lds(kdma + base + st * TPI * tok + kcol[st], dst + st * 1024);
+#pragma unroll
+    for (int r = 0; r < VI; ++r) stream_to_lds(vdma + base + r * TPI * tok, dst + KBYTES + r * 1024);
+  };
+  // score operand: lane l reads token l16, chunk j*(DL/8) + st
+  int kread[KSTEP];
+#pragma unroll
+  for (int st = 0; st < KSTEP; ++st)
+    kread[st] = l16 * 2 * D + 16 * ((j * (DL / 8) + st) ^ kswz<VCH>(l16));
 
   float m[GB];          // running max per head, log2 domain (wave-uniform)
-  float o[GB][8];       // this lane's slice of O for each head
+  float o[GB][VPL];     // this lane's d values of O for each head
 #pragma unroll
   for (int h = 0; h < GB; ++h) {
     m[h] = neg_inf();
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+    for (int e = 0; e < VPL; ++e) o[h][e] = 0.f;
   }
   float l_lane = 0.f;   // share of the row sum of head l16 (tokens of this lane)
 
-  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
-  const int64_t tok = (int64_t)p.Hkv * D;  // elements between tokens of a page
-  const uint16_t* kpool = (const uint16_t*)p.k_pool + (int64_t)g * D + j * DL + l16 * tok;
-  const uint16_t* vpool = (const uint16_t*)p.v_pool + (int64_t)g * D + c * 8 + tg * tok;
-
-  uint4 kc[KSTEP], vc[VI], kn[KSTEP], vn[VI];
-  auto load_page = [&](int pg, uint4* kk, uint4* vv) {
-    const int64_t base = (int64_t)pt[pg] * kPage * tok;
-#pragma unroll
-    for (int st = 0; st < KSTEP; ++st) kk[st] = *(const uint4*)(kpool + base + 8 * st);
-#pragma unroll
-    for (int r = 0; r < VI; ++r) vv[r] = *(const uint4*)(vpool + base + r * TPI * tok);
-  };
-  load_page(pg0, kc, vc);
+  issue_page(pg0, 0);
+  if (NSLOT == 2 && pg0 + 1 < pg1) issue_page(pg0 + 1, 1);
 
   for (int pg = pg0; pg < pg1; ++pg) {
-    if (pg + 1 < pg1) load_page(pg + 1, kn, vn);
+    const int slot = NSLOT == 2 ? ((pg - pg0) & 1) : 0;
+    if (NSLOT == 2 && pg + 1 < pg1) wait_loads<NLOAD>();
+    else wait_loads<0>();
+    const char* sp = ring_ptr + slot * SLOT;
+    uint4 kf[KSTEP];
+#pragma unroll
+    for (int st = 0; st < KSTEP; ++st) kf[st] = *(const uint4*)(sp + kread[st]);
+    uint32_t vr[kPage];
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) {
+      if constexpr (VPL == 2) vr[t] = *(const uint32_t*)(sp + KBYTES + t * 2 * D + 4 * lane);
+      else vr[t] = *(const uint16_t*)(sp + KBYTES + t * 2 * D + 2 * lane);
+    }
+    wait_lds_reads();
+    if (pg + NSLOT < pg1) issue_page(pg + NSLOT, slot);
+
     const int tok0 = pg * kPage;
+    // slots past the sequence end may hold anything (NaN): zero their V
+    if (tok0 + kPage > L) {
+#pragma unroll
+      for (int t = 0; t < kPage; ++t)
+        if (tok0 + t >= L) vr[t] = 0u;
+    }
 
     // ---- scores S[token][head] on the matrix cores ----
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < KSTEP; ++st) acc = Mma16<T>::mma(kc[st], qf[st], acc);
+    for (int st = 0; st < KSTEP; ++st) acc = Mma16<T>::mma(kf[st], qf[st], acc);
     float sc[4];
     float mx = neg_inf();
 #pragma unroll
@@ -163,118 +256,132 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
         const float alpha = fast_exp2(m[h] - pm);
         m[h] = pm;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+        for (int e = 0; e < VPL; ++e) o[h][e] *= alpha;
         if (l16 == h) a_sel = alpha;
       }
       if (l16 == h) m_sel = m[h];
     }
     l_lane *= a_sel;
 
-    // ---- probabilities -> LDS ----
-    float* pl = p_lds[pg & 1];
+    float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float pr = (sc[i] == neg_inf()) ? 0.f : fast_exp2(sc[i] - m_sel);
-      l_lane += pr;
-      if (l16 < GB) pl[(4 * j + i) * GB + l16] = pr;
+      pr[i] = (sc[i] == neg_inf()) ? 0.f : fast_exp2(sc[i] - m_sel);
+      l_lane += pr[i];
     }
-    __syncthreads();
 
-    // ---- O += P V on the vector ALUs ----
+    // ---- O += P V: P[t][h] sits in register t%4 of lane 16(t/4) + h ----
 #pragma unroll
-    for (int r = 0; r < VI; ++r) {
-      const int t = tg + r * TPI;
-      const bool ok = tok0 + t < L;
-      float pv[GB];
+    for (int t = 0; t < kPage; ++t) {
+      float v[VPL];
+      v[0] = E::lo(vr[t]);
+      if constexpr (VPL == 2) v[1] = E::hi(vr[t]);
 #pragma unroll
-      for (int h = 0; h < GB; ++h) pv[h] = pl[t * GB + h];
+      for (int h = 0; h < GB; ++h) {
+        const float w = lane_value(pr[t & 3], 16 * (t >> 2) + h);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x = ok ? comp(vc[r], w) : 0u;
-        const float v0 = E::lo(x), v1 = E::hi(x);
-#pragma unroll
-        for (int h = 0; h < GB; ++h) {
-          o[h][2 * w] = fmaf(pv[h], v0, o[h][2 * w]);
-          o[h][2 * w + 1] = fmaf(pv[h], v1, o[h][2 * w + 1]);
-        }
+        for (int e = 0; e < VPL; ++e) o[h][e] = fmaf(w, v[e], o[h][e]);
       }
     }
-
-#pragma unroll
-    for (int st = 0; st < KSTEP; ++st) kc[st] = kn[st];
-#pragma unroll
-    for (int r = 0; r < VI; ++r) vc[r] = vn[r];
   }
 
-  // ---- merge token groups (same running max everywhere: plain sums) ----
-#pragma unroll
-  for (int x = VCH; x < 64; x <<= 1)
-#pragma unroll
-    for (int h = 0; h < GB; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] += xor_lane(o[h][e], x);
   l_lane += xor_lane(l_lane, 16);
   l_lane += xor_lane(l_lane, 32);
-
 #pragma unroll
   for (int h = 0; h < GB; ++h) {
     const float lt = lane_value(l_lane, h);
     const int64_t row = ((int64_t)b * p.Hq + h0 + h) * p.max_splits + s;
-    if (tg == 0) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      float* dst = p.o_part + row * D + c * 8;
-      *(float4*)dst = make_float4(o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv);
-      *(float4*)(dst + 4) = make_float4(o[h][4] * inv, o[h][5] * inv, o[h][6] * inv, o[h][7] * inv);
-    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float* dst = p.o_part + row * D + lane * VPL;
+    if constexpr (VPL == 2) *(float2*)dst = make_float2(o[h][0] * inv, o[h][1] * inv);
+    else *dst = o[h][0] * inv;
     if (lane == 0) p.lse_part[row] = lt > 0.f ? (m[h] + __builtin_log2f(lt)) * kLn2 : neg_inf();
   }
 }
 
+// Split merge for one (sequence, query head), 256 threads: thread (sg, q)
+// with sg = tid / 32 in 0..7 and q = tid % 32 accumulates the d values
+// q*D/32 .. of splits sg, sg+8, ...; the eight partial sums are then added
+// through LDS. The max and the sum of exp over the split log-sum-exps are
+// taken by every wave in parallel over lanes (64 splits per pass).
+constexpr int kCombineThreads = 256;
+constexpr int kCombineGroups = kCombineThreads / 32;
+
 template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeParams p) {
   using E = Elem<T>;
-  constexpr int PER = D / 64;  // head-dim values per lane
+  constexpr int PER = D / 32;  // d values per thread (one 8- or 16-byte load per split)
+  static_assert(PER == 2 || PER == 4, "combine layout");
+  __shared__ float part[kCombineGroups][D];
   const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int sg = tid >> 5, q = tid & 31;
   const int L = p.seq_lens[b];
   const int npages = (L + kPage - 1) / kPage;
   const int ns = (npages + p.pages_per_split - 1) / p.pages_per_split;
   const int64_t row = ((int64_t)b * p.Hq + h) * p.max_splits;
   const float* lp = p.lse_part + row;
-  const float* op = p.o_part + row * D;
+  const float* op = p.o_part + row * D + q * PER;
 
   float mx = neg_inf();
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, lp[s]);
+  for (int s0 = 0; s0 < ns; s0 += 64)
+    if (s0 + lane < ns) mx = fmaxf(mx, lp[s0 + lane]);
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) mx = fmaxf(mx, xor_lane(mx, x));
+  float sum = 0.f;
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  float sum = 0.f;
   if (mx != neg_inf()) {
-    for (int s = 0; s < ns; ++s) {
-      const float w = fast_exp2((lp[s] - mx) * kLog2e);
-      sum += w;
+    for (int s0 = 0; s0 < ns; s0 += 64)
+      if (s0 + lane < ns) sum += fast_exp2((lp[s0 + lane] - mx) * kLog2e);
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, op[(int64_t)s * D + lane + 64 * i], acc[i]);
+    for (int x = 1; x < 64; x <<= 1) sum += xor_lane(sum, x);
+#pragma unroll 4
+    for (int s = sg; s < ns; s += kCombineGroups) {
+      const float w = fast_exp2((lp[s] - mx) * kLog2e);
+      if constexpr (PER == 4) {
+        const float4 v = *(const float4*)(op + (int64_t)s * D);
+        acc[0] = fmaf(w, v.x, acc[0]);
+        acc[1] = fmaf(w, v.y, acc[1]);
+        acc[2] = fmaf(w, v.z, acc[2]);
+        acc[3] = fmaf(w, v.w, acc[3]);
+      } else {
+        const float2 v = *(const float2*)(op + (int64_t)s * D);
+        acc[0] = fmaf(w, v.x, acc[0]);
+        acc[1] = fmaf(w, v.y, acc[1]);
+      }
     }
   }
-  const float inv = sum > 0.f ? 1.f / sum : 0.f;
-  uint16_t* dst = (uint16_t*)p.o + ((int64_t)b * p.Hq + h) * D;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const uint32_t w = E::pack2(acc[i] * inv, 0.f);
-    dst[lane + 64 * i] = (uint16_t)(w & 0xffffu);
+  for (int i = 0; i < PER; ++i) part[sg][q * PER + i] = acc[i];
+  __syncthreads();
+  if (tid < D / 2) {
+    // thread tid finishes d values 2 tid, 2 tid + 1 in fixed group order
+    float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+    for (int g = 0; g < kCombineGroups; ++g) {
+      r0 += part[g][2 * tid];
+      r1 += part[g][2 * tid + 1];
+    }
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    uint32_t* dst = (uint32_t*)((uint16_t*)p.o + ((int64_t)b * p.Hq + h) * D);
+    dst[tid] = E::pack2(r0 * inv, r1 * inv);
   }
-  if (lane == 0)
+  if (tid == 0)
     p.lse[(int64_t)b * p.Hq + h] = sum > 0.f ? mx + __builtin_logf(sum) : neg_inf();
 }
 
 template <typename T, int D, int GB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t st) {
-  const dim3 grid_split(p.max_splits, p.Hkv * (p.group / GB), p.B);
-  hipLaunchKernelGGL((decode_split_kernel<T, D, GB>), grid_split, dim3(64), 0, st, p);
+  const int64_t items = (int64_t)p.B * p.max_splits * p.Hkv * (p.group / GB);
+  const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, GB>), dim3(blocks), dim3(64 * kWavesPerBlock), 0,
+                     st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(p.Hq, p.B), dim3(64), 0, st, p);
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(p.Hq, p.B), dim3(kCombineThreads), 0, st,
+                     p);
   return hipGetLastError();
 }
 

@@ -71,4 +71,31 @@ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Byte address of a __shared__ object in the LDS aperture.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Direct global -> LDS 16-byte load (global_load_lds_dwordx4): lane i of
+// the wave writes LDS bytes [lds_wave_base + 16 i, +16); lds_wave_base is a
+// wave-uniform LDS byte address (goes to M0). Written as inline assembly so
+// that the compiler's wait-count pass does not treat every later LDS read as
+// possibly aliasing it; completion is awaited explicitly with s_waitcnt
+// vmcnt by the caller before the LDS bytes are read.
+__device__ __forceinline__ void load_to_lds(const void* gsrc, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(lds_wave_base)
+               : "memory", "m0");
+}
+
+// The same copy with the non-temporal hint, for bytes that are read once
+// (streamed K/V pages): they do not displace cache lines that are reused.
+__device__ __forceinline__ void stream_to_lds(const void* gsrc, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(gsrc), "s"(lds_wave_base)
+               : "memory", "m0");
+}
+
 }  // namespace fa

@@ -122,19 +122,6 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* lds_byte_ptr) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// Direct global -> LDS 16-byte load (global_load_lds_dwordx4): lane i of
-// the wave writes LDS bytes [lds_wave_base + 16 i, +16); lds_wave_base is a
-// wave-uniform LDS byte address (goes to M0). Written as inline assembly so
-// that the compiler's wait-count pass does not treat every later LDS read as
-// possibly aliasing it; completion is awaited explicitly with s_waitcnt
-// vmcnt before the workgroup barrier that publishes the tile.
-__device__ __forceinline__ void load_to_lds(const void* gsrc, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gsrc), "s"(lds_wave_base)
-               : "memory", "m0");
-}
-
 // Keep a value's computation ahead of this point: the empty volatile asm
 // "uses" it, and the compiler does not move volatile asm across the
 // scheduling fences that lay out the MFMA/softmax overlap.
@@ -143,9 +130,6 @@ __device__ __forceinline__ void pin(uint4& x) {
   asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
 }
 
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {

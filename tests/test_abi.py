@@ -108,4 +108,6 @@ def test_workspace_size(lib):
     assert f(64, 32, 128, 2017, 16, 0) == 64 * 32 * 64 * 129 * 4
     assert f(2, 4, 64, 10, 16, 3) == 2 * 4 * 3 * 65 * 4        # ceil(10/3)=4 pages -> 3 splits
     assert f(2, 4, 64, 10, 16, 1) == 2 * 4 * 1 * 65 * 4
+    # a split holds at most 64 pages: one split over 200 pages becomes 4
+    assert f(1, 1, 128, 200, 16, 1) == 1 * 1 * 4 * 129 * 4
     assert f(0, 4, 64, 10, 16, 1) == 0 and f(2, 4, 64, 10, 16, 11) == 0
