@@ -13,6 +13,11 @@ time of the timed steps divided by their number.
 The CPU baseline is the fp64 oracle run on a bounded sample of the same
 prefill workload (whole heads, every row) on this host's cores.
 
+``roofline.traffic`` is the HBM bytes per call from rocprofv3 FETCH_SIZE and
+WRITE_SIZE counters calibrated on a copy of known size, as recorded in
+profiles/hbm_traffic.txt; it is null when the kernel sources no longer
+match the ones those counters were taken on.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -33,6 +38,43 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+CSRC = os.path.join(ROOT, "io_aware_exact_flashattention_amd", "csrc")
+KERNEL_SOURCES = {
+    "prefill": ["fa_fwd.hip", "fa_device.h", "fa_internal.h", "fa_api.cpp"],
+    "decode": ["fa_decode.hip", "fa_device.h", "fa_internal.h", "fa_api.cpp"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def sources_sha256(which: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[which]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(which: str):
+    """HBM bytes per call (FETCH_SIZE + WRITE_SIZE, calibrated against a copy
+    of known size) recorded for the current kernel sources; None when the
+    sources changed since the counters were taken, or none were taken."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    sha = sources_sha256(which)
+    for ln in lines:
+        if not ln.startswith("path="):
+            continue
+        kv = dict(f.split("=", 1) for f in ln.split())
+        if kv.get("path") == which and kv.get("sources_sha256") == sha:
+            return {"bytes_per_call": int(kv["hbm_bytes_per_call"]),
+                    "fetch_bytes": int(kv["fetch_bytes_per_call"]),
+                    "write_bytes": int(kv["write_bytes_per_call"])}
+    return None
 
 
 def cpu_baseline(x, heads: int):
@@ -64,7 +106,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2)
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
@@ -167,17 +209,21 @@ def main():
         tflops = pre_flops / (avg * 1e-3) / 1e12
         out["value"] = tflops
         out["prefill_ms"] = {"mean": avg, "median": float(np.median(pre_ms)), "min": float(np.min(pre_ms))}
+        tr = measured_traffic("prefill")
         out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                           "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                           "traffic": tr["bytes_per_call"] if tr else None,
                            "kernel": "fwd_mfma_kernel<Bf16,128,causal>"}
     if do_dec:
         avg = float(np.mean(dec_ms))
+        tr_dec = measured_traffic("decode")
         gbs = kv_bytes / (avg * 1e-3) / 1e9
         out["decode"] = {
             "value": gbs, "unit": "GB/s", "kv_bytes_per_call": kv_bytes,
             "ms": {"mean": avg, "median": float(np.median(dec_ms)), "min": float(np.min(dec_ms))},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                         "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": tr_dec["bytes_per_call"] if tr_dec else None,
                          "kernel": "decode_split_kernel + decode_combine_kernel"},
         }
     if args.copy_probe_mb:
