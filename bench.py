@@ -49,11 +49,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
 def sources_sha256(which: str) -> str:
+    """SHA-256 of the path's source files with comments and whitespace
+    removed, so that editing a comment does not retire recorded counters."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[which]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update(re.sub(r"\s+", "", src).encode())
     return h.hexdigest()
 
 

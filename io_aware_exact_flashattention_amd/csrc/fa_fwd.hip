@@ -9,22 +9,31 @@
 // registers; device memory sees Q, K, V read and O, LSE written.
 //
 // gfx950 mapping of the 16-bit path (fwd_mfma_kernel):
-//  * 4 wavefronts x 32 query rows = 128-row Q tile; K/V tiles of 64 keys.
+//  * A workgroup owns a 256-row Q tile: 8 wavefronts x 32 query rows, two
+//    per SIMD; K/V tiles of 64 keys.
 //  * Scores are formed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_{bf16,f16}: the Q fragment is the B operand held in
 //    VGPRs for the whole loop, K rows come from LDS as the A operand. In the
 //    32x32 result a lane owns one query (lane % 32) and 16 of the 32 keys, so
 //    a row max / row sum is a per-lane reduction plus one exchange with
-//    lane ^ 32 - no LDS and no atomics.
+//    lane ^ 32 - no LDS traffic for the softmax, no atomics.
 //  * The same lane layout is exactly the B operand of O^T += V^T P^T, so the
-//    probabilities go from the score accumulator to the second MFMA after a
-//    round-to-nearest conversion to 16 bits, without leaving the lane.
-//  * V is stored transposed in LDS (V^T, keys permuted to match the lane
-//    layout of P), written from two key rows at a time as packed pairs.
-//  * K and V^T tiles are double-buffered in LDS: the global loads of tile
-//    j+1 are in flight while tile j is multiplied; one barrier per tile.
-//  * LDS rows are XOR-swizzled in 16-byte chunks so that the 32 rows read
-//    by one MFMA operand fall in distinct banks.
+//    probabilities go from the score registers to the second MFMA after a
+//    round-to-nearest conversion to 16 bits, without leaving the lane. The
+//    V^T operand is read from the row-major V tile with ds_read_b64_tr_b16.
+//  * K and V tiles reach LDS by direct-to-LDS global loads (no register
+//    round trip) into two 3-slot rings; each tile is loaded two phases
+//    before it is read. LDS rows are XOR-swizzled in 16-byte chunks so that
+//    the rows read by one MFMA operand fall in distinct banks.
+//  * The two waves of a SIMD run in counter-phase: while one multiplies
+//    (P.V of tile j and the scores of tile j+1: MFMAs and LDS reads only),
+//    the other computes the softmax of its tile (vector ALUs only), and a
+//    workgroup barrier separates the phases. The matrix core and the vector
+//    ALUs of the SIMD are then busy at the same time.
+//  * The running max is a reference raised only when a tile exceeds it by
+//    more than 2^8 (weights stay below 2^8 in fp32), so most tiles skip the
+//    rescale of the output accumulator; numerator and denominator share the
+//    reference, so the result equals the exact running-max recurrence.
 //  * Workgroup ids are remapped so that each XCD (workgroups are dealt out
 //    round-robin over the 8 XCDs) gets a contiguous run of (sequence, head)
 //    units, keeping a head's K/V in that XCD's L2; inside a head the query
@@ -44,11 +53,13 @@ constexpr int kBM = 256;      // query rows per workgroup, 16-bit path (8 waves 
 constexpr int kBN = 64;       // keys per K/V tile, 16-bit path
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kStages = 4;    // LDS ring of K/V tiles
+constexpr int kKStages = 3;   // LDS ring of K tiles
+constexpr int kVStages = 3;   // LDS ring of V tiles
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maximum.
 constexpr int kWaitVmcnt0 = 0x0F70;
-// s_waitcnt immediate: vmcnt(n) for n < 16, expcnt and lgkmcnt at their maximum.
-constexpr int wait_vmcnt(int n) { return 0x0F70 | n; }
+// s_waitcnt immediate: vmcnt(n) (n < 64; bits 3:0 and 15:14), expcnt and
+// lgkmcnt at their maximum.
+constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // Rescale threshold of the running max (log2 units): weights stay <= 2^8.
 constexpr float kRescale = 8.f;
 
@@ -117,7 +128,8 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // ds_read_b64_tr_b16. Inside each group of 16 lanes, lane j receives element
 // j%4 of the 8 bytes addressed by lane 4e + j/4, as its element e.
-__device__ __forceinline__ uint2 lds_read_tr(const char* lds_byte_ptr) {
+typedef __attribute__((address_space(3))) const char lds_cchar;
+__device__ __forceinline__ uint2 lds_read_tr(lds_cchar* lds_byte_ptr) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_byte_ptr);
   return __builtin_bit_cast(uint2, v);
 }
@@ -129,22 +141,24 @@ __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint4& x) {
   asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
 }
+__device__ __forceinline__ void pin16(f32x16& x) { asm volatile("" : "+v"(x)); }
 
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   using E = Elem<T>;
   using G = TileGeom<D>;
-  constexpr int KS = D / 16;    // MFMA k-steps of Q K^T
-  constexpr int DB = D / 32;    // 32-row blocks of O^T
-  constexpr int NB = kBN / 32;  // 32-key blocks per tile
-  constexpr int LD = G::LOADS;
-  constexpr int TILE_LOADS = 2 * LD;             // K and V loads per lane per tile
-  constexpr int STAGE = 2 * G::BYTES;            // one K tile then one V tile
+  constexpr int KS = D / 16;        // MFMA k-steps of Q K^T (= chunks of a step)
+  constexpr int DB = D / 32;        // 32-row blocks of O^T
+  constexpr int NB = kBN / 32;      // 32-key blocks per tile
+  constexpr int LD = G::LOADS;      // 16-byte loads per lane per K (or V) tile
+  constexpr int PV_N = DB * NB * 2; // P.V MFMAs per tile
+  static_assert(PV_N == 2 * KS && NB == 2, "one score k-step (two MFMAs) per two P.V MFMAs");
 
-  // Ring of kStages (K, V) tile pairs. Tile j lives in stage j % kStages; it
-  // is loaded two steps before its keys are first used.
-  __shared__ __attribute__((aligned(16))) char lds[kStages * STAGE];
+  // K ring (kKStages tiles), then V ring (kVStages tiles). At step j the
+  // K tile j+3 and the V tile j+1 are loaded, so every tile has two steps
+  // to land: step j reads K of tile j+1 and V of tile j-1.
+  __shared__ __attribute__((aligned(16))) char lds[(kKStages + kVStages) * G::BYTES];
 
   const Work w = map_block(p.n_qtiles, p.Hq);
   int q0, Lq, k0, Lk;
@@ -164,6 +178,16 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
 
   const int wrow0 = row0 + wave * 32;
   const int my_row = wrow0 + l32;
+
+  if (n_kv == 0) {  // no row of the tile sees a key: O = 0, LSE = -inf
+    if (my_row < Lq) {
+      uint16_t* dst = (uint16_t*)p.o + (int64_t)(q0 + my_row) * p.q_row + (int64_t)w.h * D;
+#pragma unroll
+      for (int c = hh; c < D / 8; c += 2) *(uint4*)(dst + 8 * c) = make_uint4(0, 0, 0, 0);
+      if (hh == 0) p.lse[(int64_t)(q0 + my_row) * p.Hq + w.h] = neg_inf();
+    }
+    return;
+  }
 
   // Q fragment: B operand of S^T = K Q^T. Lane (l32, hh) holds
   // Q[my_row][16s + 8hh .. +7] for every k-step s.
@@ -197,17 +221,35 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   const uint32_t lds0 = lds_address(lds);
   const uint32_t lds_wave = lds0 + wave * 64 * 16;
 
-  auto issue_tile = [&](int j) {
-    const uint32_t st = lds_wave + (j % kStages) * STAGE;
+  // Tiles past the last one are loaded too (rows clamped to the last key,
+  // into ring slots no longer read), so every step issues and awaits the
+  // same number of loads.
+  auto issue_k = [&](int j) {
+    const uint32_t st = lds_wave + (j % kKStages) * G::BYTES;
 #pragma unroll
     for (int n = 0; n < LD; ++n) {
-      // rows past the sequence end repeat its last row (finite values that
-      // the mask gives weight zero)
       const int64_t key = min(j * kBN + ld_row[n], last_key);
       load_to_lds(kbase + key * p.kv_row + k_col[n], st + n * kThreads * 16);
-      load_to_lds(vbase + key * p.kv_row + v_col[n], st + G::BYTES + n * kThreads * 16);
     }
   };
+  auto issue_v = [&](int j) {
+    const uint32_t st = lds_wave + (kKStages + j % kVStages) * G::BYTES;
+#pragma unroll
+    for (int n = 0; n < LD; ++n) {
+      const int64_t key = min(j * kBN + ld_row[n], last_key);
+      load_to_lds(vbase + key * p.kv_row + v_col[n], st + n * kThreads * 16);
+    }
+  };
+  // Slot byte offsets inside the LDS array (K ring, then V ring). Passed
+  // through readfirstlane so that loop strength reduction does not turn
+  // every fragment address into an induction variable of its own.
+  auto k_stage = [&](int j) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((j % kKStages) * G::BYTES);
+  };
+  auto v_stage = [&](int j) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((kKStages + j % kVStages) * G::BYTES);
+  };
+  lds_cchar* const L = (lds_cchar*)lds;
 
   // ---- per-lane LDS read offsets (bytes, inside a tile) ----
   // K, A operand of S^T: row 32kb + l32, logical chunk 2s + hh. The kb term
@@ -227,8 +269,22 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     const int gran = 8 * db + 4 * ((lane >> 4) & 1) + (vi & 3);  // 8-byte granule of the row
-    v_off[db] = G::BYTES + v_row * G::ROWB + 16 * ((gran >> 1) ^ G::v_swz(v_row)) + 8 * (gran & 1);
+    v_off[db] = v_row * G::ROWB + 16 * ((gran >> 1) ^ G::v_swz(v_row)) + 8 * (gran & 1);
   }
+  // P.V MFMA m of a tile (m = 0 .. PV_N-1): probabilities block (kb, u) =
+  // m / DB (outer, so each P fragment dies after its DB MFMAs), d-block m % DB.
+  auto v_frag = [&](uint32_t vst, int m) {
+    const int pidx = m / DB, db = m % DB;
+    lds_cchar* vq = L + (vst + v_off[db]) + (32 * (pidx / 2) + 16 * (pidx % 2)) * G::ROWB;
+    const uint2 lo = lds_read_tr(vq);
+    const uint2 hi = lds_read_tr(vq + 8 * G::ROWB);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
+  auto k_frag = [&](uint32_t kst, int st, int kb) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(L + (kst + k_off[st]) + kb * 32 * G::ROWB);
+    return __builtin_bit_cast(uint4, v);
+  };
 
   f32x16 acc_o[DB];
 #pragma unroll
@@ -244,148 +300,166 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   float l_run = 0.f;        // this lane's share of the running row sum
   const float c2 = p.scale_log2;
 
-  // scores of tile j (s_cur) and of tile j+1 (s_nxt)
-  f32x16 s_cur[NB], s_nxt[NB];
-  auto scores = [&](const char* stage, f32x16* acc) {
+  // ---- two groups of waves in counter-phase ----
+  // Waves 0-3 (group 0) and 4-7 (group 1) sit one per SIMD, so every SIMD
+  // holds one wave of each group. A wave alternates a softmax phase (vector
+  // ALUs only: probabilities of tile j) and a matrix phase (P.V of tile j
+  // and the scores of tile j+1: MFMAs and LDS reads only). Group 1 runs one
+  // phase behind group 0, and every phase boundary is a workgroup barrier,
+  // so on each SIMD one wave keeps the matrix core busy while the other
+  // computes its softmax.
+  //   slot 2j:   group 0 softmax(j),  group 1 matrix(j-1) (scores of tile 0 for j = 0)
+  //   slot 2j+1: group 0 matrix(j),   group 1 softmax(j)
+  // Loads: the barrier opening slot 2j+1 waits for K tile j+1 and V tile j
+  // (issued two slots earlier) and issues K tile j+2 and V tile j+1.
+  const int grp = wave >> 2;
+  f32x16 sc[NB];   // scores of the tile being worked on
+  uint4 pf[NB][2]; // its probabilities, B operand of O^T += V^T P^T
+
+  // Matrix phase: P.V of tile j and the scores of tile j+1, as KS groups
+  // of "two P.V MFMAs + one k-step (NB MFMAs) of the scores". The LDS
+  // fragments of group g+1 are read while group g multiplies (two register
+  // buffers); fences keep the compiler from hoisting more reads than that.
+  // (After the last tile the "next scores" come from a stale slot and are
+  // never used.)
+  auto matrix = [&](int j) {
+    const uint32_t vst = v_stage(j);
+    const uint32_t kst = k_stage(j + 1);
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+    uint4 vf[2][2], kf[2][NB];
+    auto load_group = [&](int g, int buf) {
+      vf[buf][0] = v_frag(vst, 2 * g);
+      vf[buf][1] = v_frag(vst, 2 * g + 1);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const char* kp = stage + k_off[s];
+      for (int kb = 0; kb < NB; ++kb) kf[buf][kb] = k_frag(kst, g, kb);
+    };
+    __builtin_amdgcn_s_setprio(1);
+    load_group(0, 0);
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
-        const uint4 a = *(const uint4*)(kp + kb * 32 * G::ROWB);
-        acc[kb] = E::mma32(a, qf[s], acc[kb]);
-      }
-      // bound the K fragments held in registers (two k-steps in flight)
-      if (s % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // ---- prologue: tiles 0..2 in flight, scores of tile 0 ----
-  for (int j = 0; j < min(n_kv, kStages - 1); ++j) issue_tile(j);
-  if (n_kv > 2) __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * TILE_LOADS));
-  else if (n_kv > 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(TILE_LOADS));
-  else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  if (n_kv > 0) scores(lds, s_cur);
-
-  // One pipeline step: the softmax and P.V of tile j, plus the scores of
-  // tile j+1. The score MFMAs of tile j+1 and the softmax of tile j are
-  // independent; they are laid out as KS chunks, each "read the next K
-  // fragments, two MFMAs, a slice of the softmax", fenced so the compiler
-  // keeps that order: the matrix core works on the MFMAs while the vector
-  // ALUs work on the softmax slice.
-  auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt) {
-    const char* st_cur = lds + (j % kStages) * STAGE;
-    const char* st_nxt = lds + ((j + 1) % kStages) * STAGE;
-    // tile j+1 has landed for every wave, and every wave is done with the
-    // stage that tile j+3 goes to (it held tile j-1)
-    if (j + 2 < n_kv) __builtin_amdgcn_s_waitcnt(wait_vmcnt(TILE_LOADS));
-    else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (j + 3 < n_kv) issue_tile(j + 3);
-
-    // ---- mask keys past the sequence end / above the diagonal ----
-    const bool need_mask = (j * kBN + kBN > Lk) || (CAUSAL && (j * kBN + kBN - 1 > wrow0 + delta));
-    if (need_mask) {
-      const int lim = CAUSAL ? min(Lk - 1, my_row + delta) : Lk - 1;
+    for (int g = 0; g < KS; ++g) {
+      if (g + 1 < KS) load_group(g + 1, (g + 1) & 1);
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j * kBN + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key > lim) s_cur[kb][r] = neg_inf();
-        }
-    }
-
-    // ---- S_{j+1} = K_{j+1} Q^T  ||  online softmax of tile j ----
-    // (past the last tile the next stage holds stale data; those scores are
-    // never used)
-    constexpr int MAXC = KS / 2;       // chunks that reduce the row max
-    constexpr int EXPC = KS - MAXC;    // chunks that exponentiate
-    constexpr int GROUPS = 2 * NB;     // groups of 8 probabilities
-    constexpr int PER_MAX = 16 * NB / MAXC;
-    constexpr int PER_EXP = GROUPS / EXPC;
-    static_assert(PER_EXP >= 1 && GROUPS % EXPC == 0 && (16 * NB) % MAXC == 0, "chunking");
-    uint4 kfr[2][NB];
-    uint4 pf[NB][2];
-    float mx = neg_inf(), rs = 0.f, alpha = 1.f, base = 0.f;
-    bool raise = false;
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s_nxt[kb][r] = 0.f;
-      kfr[0][kb] = *(const uint4*)(st_nxt + k_off[0] + kb * 32 * G::ROWB);
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (s + 1 < KS) {
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-          kfr[(s + 1) & 1][kb] = *(const uint4*)(st_nxt + k_off[s + 1] + kb * 32 * G::ROWB);
-      }
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb) s_nxt[kb] = E::mma32(kfr[s & 1][kb], qf[s], s_nxt[kb]);
-      if (s < MAXC) {
-#pragma unroll
-        for (int i = s * PER_MAX; i < (s + 1) * PER_MAX; ++i) mx = fmaxf(mx, s_cur[i / 16][i % 16]);
-        if (s == MAXC - 1) mx = fmaxf(mx, xor_lane(mx, 32));
-        pin(mx);
-      } else {
-        if (s == MAXC) {
-          const float mx2 = mx * c2;  // -inf when the row sees no key of this tile
-          raise = mx2 > m_run + kRescale;
-          alpha = fast_exp2(raise ? m_run - mx2 : 0.f);  // exp2(0) = 1
-          m_run = raise ? mx2 : m_run;
-          base = (m_run == neg_inf()) ? 0.f : m_run;
-        }
-#pragma unroll
-        for (int gi = (s - MAXC) * PER_EXP; gi < (s - MAXC + 1) * PER_EXP; ++gi) {
-          const int kb = gi / 2, u = gi % 2;
-          float e[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            e[i] = fast_exp2(fmaf(s_cur[kb][8 * u + i], c2, -base));
-            rs += e[i];
-          }
-          pf[kb][u] = make_uint4(E::pack2(e[0], e[1]), E::pack2(e[2], e[3]),
-                                 E::pack2(e[4], e[5]), E::pack2(e[6], e[7]));
-          pin(pf[kb][u]);
-        }
+      for (int h = 0; h < 2; ++h) {
+        const int m = 2 * g + h, pidx = m / DB;
+        acc_o[m % DB] = E::mma32(vf[g & 1][h], pf[pidx / 2][pidx % 2], acc_o[m % DB]);
+        sc[h] = E::mma32(kf[g & 1][h], qf[g], sc[h]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    l_run = l_run * alpha + rs;
+    __builtin_amdgcn_s_setprio(0);
+    // results complete before the barrier that ends the phase
+#pragma unroll
+    for (int db = 0; db < DB; ++db) pin16(acc_o[db]);
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) pin16(sc[kb]);
+  };
+
+  auto softmax = [&](int j) {
+    const bool need_mask = (j * kBN + kBN > Lk) || (CAUSAL && (j * kBN + kBN - 1 > wrow0 + delta));
+    if (need_mask) {
+      // key of register r of block kb: j*kBN + 4hh + (32kb + 8(r/4) + r%4);
+      // compare the constant part against one per-lane threshold
+      const int lim = CAUSAL ? min(Lk - 1, my_row + delta) : Lk - 1;
+      const int t = lim - j * kBN - 4 * hh;
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) > t) sc[kb][r] = neg_inf();
+    }
+    float mx = neg_inf();
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    const float mx2 = mx * c2;  // -inf when the row sees no key of this tile
+    const bool raise = mx2 > m_run + kRescale;
+    const float alpha = fast_exp2(raise ? m_run - mx2 : 0.f);  // exp2(0) = 1
+    m_run = raise ? mx2 : m_run;
+    const float base = (m_run == neg_inf()) ? 0.f : m_run;
     if (__ballot(raise)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
     }
-
-    // ---- O^T += V_j^T P_j^T ----
+    float rs = 0.f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const char* vp = st_cur + v_off[db];
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
+      for (int u = 0; u < 2; ++u) {
+        float e[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const char* vq = vp + (32 * kb + 16 * u) * G::ROWB;
-          const uint2 lo = lds_read_tr(vq);
-          const uint2 hi = lds_read_tr(vq + 8 * G::ROWB);
-          acc_o[db] = E::mma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pf[kb][u], acc_o[db]);
+        for (int i = 0; i < 8; ++i) {
+          e[i] = fast_exp2(fmaf(sc[kb][8 * u + i], c2, -base));
+          rs += e[i];
         }
+        pf[kb][u] = make_uint4(E::pack2(e[0], e[1]), E::pack2(e[2], e[3]),
+                               E::pack2(e[4], e[5]), E::pack2(e[6], e[7]));
+      }
+    l_run = l_run * alpha + rs;
+    // probabilities complete before the barrier that ends the phase (the
+    // compiler may not sink this arithmetic into the matrix phase)
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      pin(pf[kb][0]);
+      pin(pf[kb][1]);
     }
+    pin(l_run);
   };
 
-  for (int j = 0; j < n_kv; ++j) {
-    step(j, s_cur, s_nxt);
+  auto scores0 = [&]() {
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) s_cur[kb] = s_nxt[kb];
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) sc[kb] = E::mma32(k_frag(k_stage(0), st, kb), qf[st], sc[kb]);
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) pin16(sc[kb]);
+  };
+
+  // ---- prologue: K tiles 0, 1 and V tile 0 ----
+  issue_k(0);
+  if (n_kv > 1) issue_k(1);
+  issue_v(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (grp == 0) scores0();
+
+  // Barrier opening slot 2j+1: K tile j+1 and V tile j (issued two slots
+  // earlier) have landed for every wave, and the slots that K tile j+2 and
+  // V tile j+1 go to were last read in slot 2j-2.
+  auto odd_barrier = [&](int j) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (j + 2 < n_kv) issue_k(j + 2);
+    if (j + 1 < n_kv) issue_v(j + 1);
+  };
+  // Each group runs its own loop; both pass 2 n_kv + 1 barriers.
+  if (grp == 0) {
+    __syncthreads();  // slot 0
+    for (int j = 0; j < n_kv; ++j) {
+      softmax(j);     // slot 2j
+      odd_barrier(j);
+      matrix(j);      // slot 2j+1
+      __syncthreads();
+    }
+  } else {
+    __syncthreads();  // slot 0
+    scores0();
+    for (int j = 0; j < n_kv; ++j) {
+      odd_barrier(j);
+      softmax(j);     // slot 2j+1
+      __syncthreads();
+      matrix(j);      // slot 2j+2
+    }
   }
 
   // ---- epilogue: O = O / l, LSE = ln(sum exp) ----
@@ -531,6 +605,7 @@ __global__ __launch_bounds__(kThreads32) void fwd_f32_kernel(FwdParams p) {
 
 template <typename T, int D>
 hipError_t launch_mfma(const FwdParams& p, bool causal, int blocks, hipStream_t st) {
+
   if (causal)
     hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true>), dim3(blocks), dim3(kThreads), 0, st, p);
   else
