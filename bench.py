@@ -108,6 +108,81 @@ def cpu_baseline(x, heads: int):
                       f"fp64 NumPy, {dt:.1f} s"}
 
 
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector, published
+
+
+def other_configs(torch, fa, fi, to_dev, dev, reps=20):
+    """Throughput of the remaining parity workloads (reported, not part of
+    `value`): HIP events around each call on the current stream, after
+    warm-up calls."""
+    import numpy as np
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
+        return float(np.mean(ms)), float(np.min(ms))
+
+    def dense_case(key, x, peak, desc):
+        B, Nq, Nk, Hq, Hkv, d = x.shape
+        q, k, v = to_dev(x.q, x.dtype), to_dev(x.k, x.dtype), to_dev(x.v, x.dtype)
+        o, l = fa.fwd(q, k, v, causal=x.causal, scale=x.scale)
+        mean, mn = timed(lambda: fa.fwd(q, k, v, causal=x.causal, scale=x.scale, out=o, lse=l))
+        flops = fi.prefill_flops([Nq] * B, [Nk] * B, Hq, d, x.causal)
+        tf = flops / (mean * 1e-3) / 1e12
+        res[key] = {"workload": desc, "dtype": x.dtype, "ms_mean": mean, "ms_min": mn,
+                    "tflops": tf, "peak_tflops": peak, "frac": tf / peak}
+
+    dense_case("cfg0", fi.cfg0(), PEAK_FP32_VALU_TFLOPS,
+               "fp32 B=1 H=1 N=256 d=64, no mask (fwd_f32_kernel; launch-latency bound)")
+    dense_case("cfg1_bf16", fi.cfg1(), PEAK_BF16_TFLOPS, "causal bf16 B=4 H=16 N=2048 d=64")
+    dense_case("cfg1_bf16_qx8", fi.cfg1(q_mult=8.0), PEAK_BF16_TFLOPS,
+               "causal bf16 B=4 H=16 N=2048 d=64, Q x8 (logits to about +-45)")
+    dense_case("cfg1_f16", fi.cfg1(dtype="f16"), PEAK_BF16_TFLOPS, "causal fp16 B=4 H=16 N=2048 d=64")
+
+    x = fi.cfg3()
+    q, k, v = to_dev(x.q, x.dtype), to_dev(x.k, x.dtype), to_dev(x.v, x.dtype)
+    cq, ck = to_dev(x.cu_q, "i32"), to_dev(x.cu_k, "i32")
+    o, l = fa.fwd_varlen(q, k, v, cq, ck, x.max_q, x.max_k, causal=True, scale=x.scale)
+    mean, mn = timed(lambda: fa.fwd_varlen(q, k, v, cq, ck, x.max_q, x.max_k, causal=True,
+                                           scale=x.scale, out=o, lse=l))
+    lq = np.diff(x.cu_q)
+    flops = fi.prefill_flops(lq, np.diff(x.cu_k), x.q.shape[1], x.q.shape[2], True)
+    tf = flops / (mean * 1e-3) / 1e12
+    res["cfg3"] = {"workload": "ragged causal GQA bf16, 8 sequences U[128,4096] seed 3, Hq=32 Hkv=8 d=128",
+                   "dtype": "bf16", "ms_mean": mean, "ms_min": mn, "tflops": tf,
+                   "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
+
+    # chunked prefill over a paged cache: work = 4 Hq d x (visible query-key
+    # pairs), query i of a chunk seeing Lk - Lq + i + 1 keys
+    lq, lk = fi.chunked_prefill_lengths()
+    x = fi.paged_prefill(lq, lk, 32, 8, 128, "bf16", seed=5)
+    kv = x.kv
+    q, kp, vp = to_dev(x.q, "bf16"), to_dev(kv.k_pool, "bf16"), to_dev(kv.v_pool, "bf16")
+    cq, pt, sl = to_dev(x.cu_q, "i32"), to_dev(kv.page_table, "i32"), to_dev(kv.seq_lens, "i32")
+    o, l = fa.fwd_paged(q, kp, vp, cq, pt, sl, x.max_q, scale=kv.scale)
+    mean, mn = timed(lambda: fa.fwd_paged(q, kp, vp, cq, pt, sl, x.max_q, scale=kv.scale,
+                                          out=o, lse=l))
+    pairs = float(np.sum(lq * (lk - lq) + lq * (lq + 1) / 2))
+    tf = 4.0 * 32 * 128 * pairs / (mean * 1e-3) / 1e12
+    res["chunked_prefill_paged"] = {
+        "workload": "fa_fwd_paged: 16 chunks U[1,2048] after cached prefixes U[0,8192] seed 5, "
+                    "page 16 (permuted pool), Hq=32 Hkv=8 d=128, causal",
+        "dtype": "bf16", "ms_mean": mean, "ms_min": mn, "tflops": tf,
+        "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +191,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2)
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the throughput report of the other parity workloads")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, copy this many MiB device-to-device once (a kernel of "
                          "known traffic, to calibrate HBM byte counters)")
@@ -232,6 +309,9 @@ def main():
                          "traffic": tr_dec["bytes_per_call"] if tr_dec else None,
                          "kernel": "decode_split_kernel + decode_combine_kernel"},
         }
+    if not args.no_other:
+        log("[bench] other workloads")
+        out["other_configs"] = other_configs(torch, fa, fi, to_dev, dev)
     if args.copy_probe_mb:
         n = args.copy_probe_mb << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

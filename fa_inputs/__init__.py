@@ -275,6 +275,43 @@ def paged(lens, Hq, Hkv, d, dtype, seed, permute=True, tail_fill="zero", rng=Non
                  lens.astype(np.int32), dtype, default_scale(d), name, tail_fill)
 
 
+@dataclass
+class PagedPrefill:
+    """A ragged batch of query chunks plus a paged cache holding every key of
+    each sequence (cached prefix and the chunk itself)."""
+    q: np.ndarray              # [Tq, Hq, d]
+    cu_q: np.ndarray           # int32 [B+1]
+    kv: Paged                  # pools, page table, seq_lens and the contiguous K/V
+
+    @property
+    def max_q(self):
+        return int(np.diff(self.cu_q).max()) if len(self.cu_q) > 1 else 0
+
+
+def paged_prefill(lens_q, lens_k, Hq, Hkv, d, dtype, seed, permute=True, tail_fill="zero",
+                  name="") -> PagedPrefill:
+    """Chunked-prefill inputs: chunk s has lens_q[s] query tokens and its
+    sequence lens_k[s] >= lens_q[s] keys in the paged pool (same pool layout,
+    permutation and K/V streams as `paged`). Queries are drawn on the Q
+    stream as one packed [Tq, Hq, d] tensor."""
+    lens_q = np.asarray(lens_q, dtype=np.int64)
+    lens_k = np.asarray(lens_k, dtype=np.int64)
+    assert np.all(lens_q <= lens_k)
+    kv = paged(lens_k, Hq, Hkv, d, dtype, seed, permute=permute, tail_fill=tail_fill, name=name)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    q = _draw_q(seed, (int(cu_q[-1]), Hq, d), dtype)
+    return PagedPrefill(q, cu_q, kv)
+
+
+def chunked_prefill_lengths(seed=5, B=16):
+    """A chunked-prefill batch: cached prefixes U[0, 8192] and chunks U[1, 2048]
+    tokens (keys = prefix + chunk)."""
+    rng = np.random.default_rng(seed)
+    prefix = rng.integers(0, 8192, B, endpoint=True)
+    chunk = rng.integers(1, 2048, B, endpoint=True)
+    return chunk, prefix + chunk
+
+
 # ---------------------------------------------------- the five workloads --
 CONFIG_TEXT = (
     "single-head exact attention, no mask: B=1 H=1 Nq=Nk=256 d=64 fp32",

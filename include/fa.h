@@ -91,6 +91,34 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         int d, fa_dtype dtype, float scale, int causal, void* stream);
 
 /*
+ * fa_fwd_paged - prefill of a ragged batch of query chunks against K/V held
+ * in a paged cache ("chunked prefill").
+ * ("I/O-Aware Kernels", section "FlashInfer: I/O-aware attention for
+ * serving": ragged batches, paged KV layouts, grouped-query attention.)
+ *   q   [Tq, Hq, d] dtype, packed like fa_fwd_varlen; o [Tq, Hq, d] dtype;
+ *   lse [Tq, Hq] float32
+ *   cu_seqlens_q device int32 [B+1]: chunk s owns query rows
+ *               cu[s] .. cu[s+1]-1 (chunks may be empty)
+ *   k_pool, v_pool [num_pages, page_size, Hkv, d] dtype, page_table device
+ *               int32 [B, max_pages] and seq_lens device int32 [B] exactly
+ *               as for fa_decode_paged. seq_lens[s] counts every key of
+ *               sequence s - the cached prefix and the chunk itself, whose
+ *               K/V must already be in the pages - so the chunk's queries
+ *               are the last Lq of its Lk tokens: with causal masking, query
+ *               row i of the chunk sees keys j <= i + Lk - Lq (bottom-right).
+ *   max_seqlen_q >= every chunk length (sizes the grid).
+ * page_size must be 16, max_pages <= 8192 (sequences of at most 131072
+ * tokens), dtype FA_F16 or FA_BF16. Preconditions on the device arrays:
+ * Lq <= seq_lens[s] <= max_pages * 16, and the page-table entries of the
+ * first ceil(seq_lens[s] / 16) pages are valid page indices.
+ */
+fa_status fa_fwd_paged(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
+                       const int32_t* cu_seqlens_q, const int32_t* page_table,
+                       const int32_t* seq_lens, int B, int max_seqlen_q, int Tq, int max_pages,
+                       int num_pages, int page_size, int Hq, int Hkv, int d, fa_dtype dtype,
+                       float scale, int causal, void* stream);
+
+/*
  * fa_decode_paged_workspace_size - bytes of device workspace that
  * fa_decode_paged needs for these sizes (float32 partial outputs and
  * log-sum-exps of every split). Returns 0 for invalid sizes.

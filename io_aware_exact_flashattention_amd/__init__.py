@@ -109,6 +109,39 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: 
     return o, l
 
 
+def fwd_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+              cu_seqlens_q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+              max_seqlen_q: int, causal: bool = True, scale: float | None = None,
+              out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Chunked prefill against a paged cache. q [Tq, Hq, d] packed by
+    cu_seqlens_q (int32 [B+1]); pools [num_pages, 16, Hkv, d]; page_table
+    int32 [B, max_pages]; seq_lens int32 [B] = keys of each sequence, the
+    chunk included -> (O like q, LSE float32 [Tq, Hq])."""
+    lib = _lib.load()
+    for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("cu_seqlens_q", cu_seqlens_q),
+                 ("page_table", page_table), ("seq_lens", seq_lens)):
+        _dev_tensor(t, n)
+    _need(q.dim() == 3 and k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "bad shapes")
+    _need(q.dtype == k_pool.dtype == v_pool.dtype, "q and pools must share a dtype")
+    _need(cu_seqlens_q.dtype == torch.int32 and page_table.dtype == torch.int32
+          and seq_lens.dtype == torch.int32, "indices must be int32")
+    Tq, Hq, d = q.shape
+    num_pages, page_size, Hkv, _ = k_pool.shape
+    B = cu_seqlens_q.shape[0] - 1
+    _need(page_table.dim() == 2 and page_table.shape[0] == B and seq_lens.shape == (B,),
+          "bad index shapes")
+    if scale is None:
+        scale = default_scale(d)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _lib.check(lib.fa_fwd_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), o.data_ptr(),
+                                l.data_ptr(), cu_seqlens_q.data_ptr(), page_table.data_ptr(),
+                                seq_lens.data_ptr(), B, int(max_seqlen_q), Tq,
+                                page_table.shape[1], num_pages, page_size, Hq, Hkv, d, _dtype(q),
+                                float(scale), int(bool(causal)), _stream(q)))
+    return o, l
+
+
 def decode_workspace_size(B: int, Hq: int, d: int, max_pages: int, page_size: int = 16,
                           num_splits: int = 0) -> int:
     return int(_lib.load().fa_decode_paged_workspace_size(B, Hq, d, max_pages, page_size,

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libfa_amd.so")
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 
-EXPORTS = ("fa_status_string", "fa_version", "fa_fwd", "fa_fwd_varlen",
+EXPORTS = ("fa_status_string", "fa_version", "fa_fwd", "fa_fwd_varlen", "fa_fwd_paged",
            "fa_decode_paged_workspace_size", "fa_decode_paged")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -25,6 +25,10 @@ _SIGNATURES = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "fa_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                            _i, _f, _i, _vp]),
+    # q k_pool v_pool o lse cu_q page_table seq_lens B max_q Tq max_pages num_pages page_size
+    # Hq Hkv d dtype scale causal stream
+    "fa_fwd_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                          _i, _i, _f, _i, _vp]),
     "fa_decode_paged_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                              _f, _i, _vp, _sz, _vp]),

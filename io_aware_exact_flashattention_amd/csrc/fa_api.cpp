@@ -103,6 +103,39 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   return run_fwd(p, dtype, d, causal, max_seqlen_q, stream);
 }
 
+fa_status fa_fwd_paged(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
+                       const int32_t* cu_seqlens_q, const int32_t* page_table,
+                       const int32_t* seq_lens, int B, int max_seqlen_q, int Tq, int max_pages,
+                       int num_pages, int page_size, int Hq, int Hkv, int d, fa_dtype dtype,
+                       float scale, int causal, void* stream) {
+  fa_status st = check_common(q, k_pool, v_pool, o, lse, Hq, Hkv, d, dtype, scale);
+  if (st != FA_OK) return st;
+  if (!cu_seqlens_q || !page_table || !seq_lens) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || Tq < 0 || max_seqlen_q < 0 || max_seqlen_q > Tq) return FA_ERR_INVALID_ARG;
+  if (max_pages <= 0 || num_pages <= 0 || page_size <= 0) return FA_ERR_INVALID_ARG;
+  if (page_size != kPageSize) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (max_pages > fa::kFwdPagedMaxPages) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)num_pages * kPageSize > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (Tq == 0 || max_seqlen_q == 0) return FA_OK;  // no query rows
+  fa::FwdParams p{};
+  p.q = q; p.k = k_pool; p.v = v_pool; p.o = o; p.lse = lse;
+  p.cu_q = cu_seqlens_q; p.cu_k = nullptr;
+  p.page_table = page_table; p.seq_lens = seq_lens; p.max_pages = max_pages;
+  p.B = B; p.Nq = 0; p.Nk = 0;
+  p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.scale_log2 = scale * kLog2e;
+  p.q_row = (int64_t)Hq * d;
+  p.kv_row = (int64_t)Hkv * d;
+  const int bm = fa::fwd_block_rows(to_dt(dtype));
+  p.n_qtiles = (max_seqlen_q + bm - 1) / bm;
+  const int64_t blocks = (int64_t)p.n_qtiles * p.Hq * p.B;
+  if (blocks > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_fwd_paged(p, to_dt(dtype), d, causal != 0, (int)blocks,
+                                      (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 // Pages per split: 32 when automatic; otherwise the longest sequence is cut
 // into num_splits ranges, but a range never exceeds kMaxPagesPerSplit pages
 // (the decode kernel holds one split's page indices in the lanes of a wave).

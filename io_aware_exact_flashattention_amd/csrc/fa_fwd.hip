@@ -87,7 +87,12 @@ __device__ __forceinline__ Work map_block(int n_qtiles, int Hq) {
 
 __device__ __forceinline__ void seq_bounds(const FwdParams& p, int b, int& q0, int& Lq, int& k0,
                                            int& Lk) {
-  if (p.cu_q) {
+  if (p.seq_lens) {  // paged K/V: keys are addressed through the page table
+    q0 = p.cu_q[b];
+    Lq = p.cu_q[b + 1] - q0;
+    k0 = 0;
+    Lk = p.seq_lens[b];
+  } else if (p.cu_q) {
     q0 = p.cu_q[b];
     Lq = p.cu_q[b + 1] - q0;
     k0 = p.cu_k[b];
@@ -144,7 +149,7 @@ __device__ __forceinline__ void pin(uint4& x) {
 __device__ __forceinline__ void pin16(f32x16& x) { asm volatile("" : "+v"(x)); }
 
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   using E = Elem<T>;
   using G = TileGeom<D>;
@@ -159,6 +164,8 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   // K tile j+3 and the V tile j+1 are loaded, so every tile has two steps
   // to land: step j reads K of tile j+1 and V of tile j-1.
   __shared__ __attribute__((aligned(16))) char lds[(kKStages + kVStages) * G::BYTES];
+  // paged K/V: the sequence's page-table row
+  __shared__ int32_t pt_lds[PAGED ? kFwdPagedMaxPages : 1];
 
   const Work w = map_block(p.n_qtiles, p.Hq);
   int q0, Lq, k0, Lk;
@@ -220,6 +227,25 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   const int last_key = Lk - 1;
   const uint32_t lds0 = lds_address(lds);
   const uint32_t lds_wave = lds0 + wave * 64 * 16;
+  if (PAGED) {
+    // Stage the page indices of every key this tile may see (plain loads,
+    // completed here, before any direct-to-LDS load is counted).
+    const int32_t* pt = p.page_table + (int64_t)w.b * p.max_pages;
+    const int n_pg = (kv_end + 15) >> 4;
+    for (int i = tid; i < n_pg; i += kThreads) pt_lds[i] = pt[i];
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+  // Pool row of key `key`, clamped to the last key the tile may see (rows
+  // past it repeat that row: finite values that the mask gives weight
+  // zero). With paged K/V only the pages of keys below kv_end are staged.
+  auto key_row = [&](int key) -> int64_t {
+    if (PAGED) {
+      key = min(key, kv_end - 1);
+      return (int64_t)pt_lds[key >> 4] * 16 + (key & 15);
+    }
+    return min(key, last_key);
+  };
 
   // Tiles past the last one are loaded too (rows clamped to the last key,
   // into ring slots no longer read), so every step issues and awaits the
@@ -227,18 +253,14 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   auto issue_k = [&](int j) {
     const uint32_t st = lds_wave + (j % kKStages) * G::BYTES;
 #pragma unroll
-    for (int n = 0; n < LD; ++n) {
-      const int64_t key = min(j * kBN + ld_row[n], last_key);
-      load_to_lds(kbase + key * p.kv_row + k_col[n], st + n * kThreads * 16);
-    }
+    for (int n = 0; n < LD; ++n)
+      load_to_lds(kbase + key_row(j * kBN + ld_row[n]) * p.kv_row + k_col[n], st + n * kThreads * 16);
   };
   auto issue_v = [&](int j) {
     const uint32_t st = lds_wave + (kKStages + j % kVStages) * G::BYTES;
 #pragma unroll
-    for (int n = 0; n < LD; ++n) {
-      const int64_t key = min(j * kBN + ld_row[n], last_key);
-      load_to_lds(vbase + key * p.kv_row + v_col[n], st + n * kThreads * 16);
-    }
+    for (int n = 0; n < LD; ++n)
+      load_to_lds(vbase + key_row(j * kBN + ld_row[n]) * p.kv_row + v_col[n], st + n * kThreads * 16);
   };
   // Slot byte offsets inside the LDS array (K ring, then V ring). Passed
   // through readfirstlane so that loop strength reduction does not turn
@@ -603,13 +625,12 @@ __global__ __launch_bounds__(kThreads32) void fwd_f32_kernel(FwdParams p) {
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED = false>
 hipError_t launch_mfma(const FwdParams& p, bool causal, int blocks, hipStream_t st) {
-
   if (causal)
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true>), dim3(blocks), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true, PAGED>), dim3(blocks), dim3(kThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false>), dim3(blocks), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false, PAGED>), dim3(blocks), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
@@ -625,6 +646,20 @@ hipError_t launch_f32(const FwdParams& p, bool causal, int blocks, hipStream_t s
 }  // namespace
 
 int fwd_block_rows(Dt dt) { return dt == Dt::F32 ? kBM32 : kBM; }
+
+hipError_t launch_fwd_paged(const FwdParams& p, Dt dt, int d, bool causal, int blocks,
+                            hipStream_t st) {
+  switch (dt) {
+    case Dt::Bf16:
+      return d == 64 ? launch_mfma<Bf16, 64, true>(p, causal, blocks, st)
+                     : launch_mfma<Bf16, 128, true>(p, causal, blocks, st);
+    case Dt::F16:
+      return d == 64 ? launch_mfma<F16, 64, true>(p, causal, blocks, st)
+                     : launch_mfma<F16, 128, true>(p, causal, blocks, st);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, int blocks, hipStream_t st) {
   switch (dt) {

@@ -25,7 +25,16 @@ struct FwdParams {
   float scale_log2;  // scale * log2(e)
   int64_t q_row;     // elements between consecutive tokens of q and o (Hq * d)
   int64_t kv_row;    // elements between consecutive tokens of k and v (Hkv * d)
+  // Paged K/V (fa_fwd_paged): k and v are pools of 16-token pages, token t
+  // of sequence s lives in row page_table[s][t / 16] * 16 + t % 16; the key
+  // length of sequence s is seq_lens[s]. Null for contiguous K/V.
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int max_pages;
 };
+
+// Most page-table entries one paged prefill sequence may use (staged in LDS).
+constexpr int kFwdPagedMaxPages = 8192;
 
 // Split-KV decode over a paged cache.
 struct DecodeParams {
@@ -50,6 +59,9 @@ enum class Dt { F32, F16, Bf16 };
 hipError_t launch_fwd(const FwdParams& p, Dt dt, int d, bool causal, int grid_blocks,
                       hipStream_t stream);
 int fwd_block_rows(Dt dt);  // query rows per workgroup for this dtype
+// Prefill over a paged K/V cache (16-bit types only).
+hipError_t launch_fwd_paged(const FwdParams& p, Dt dt, int d, bool causal, int grid_blocks,
+                            hipStream_t stream);
 
 hipError_t launch_decode(const DecodeParams& p, Dt dt, int d, hipStream_t stream);
 

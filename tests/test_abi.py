@@ -111,3 +111,25 @@ def test_workspace_size(lib):
     # a split holds at most 64 pages: one split over 200 pages becomes 4
     assert f(1, 1, 128, 200, 16, 1) == 1 * 1 * 4 * 129 * 4
     assert f(0, 4, 64, 10, 16, 1) == 0 and f(2, 4, 64, 10, 16, 11) == 0
+
+
+def fwd_paged(lib, **kw):
+    a = dict(q=P, kp=P, vp=P, o=P, lse=P, cq=P, pt=P, sl=P, B=2, mq=8, Tq=16, mp=4, npg=8, ps=16,
+             Hq=4, Hkv=2, d=128, dt=2, scale=0.1, causal=1, stream=None)
+    a.update(kw)
+    return lib.fa_fwd_paged(a["q"], a["kp"], a["vp"], a["o"], a["lse"], a["cq"], a["pt"], a["sl"],
+                            a["B"], a["mq"], a["Tq"], a["mp"], a["npg"], a["ps"], a["Hq"], a["Hkv"],
+                            a["d"], a["dt"], a["scale"], a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(cq=None), 1), (dict(pt=None), 1), (dict(sl=None), 1), (dict(B=0), 1), (dict(mq=17), 1),
+    (dict(Tq=-1), 1), (dict(mp=0), 1), (dict(npg=0), 1), (dict(ps=8), 2), (dict(dt=0), 2),
+    (dict(d=96), 2), (dict(Hq=4, Hkv=3), 1), (dict(mp=8193), 2), (dict(scale=0.0), 1),
+])
+def test_fwd_paged_rejects(lib, kw, expect):
+    assert fwd_paged(lib, **kw) == expect
+
+
+def test_fwd_paged_empty_is_noop(lib):
+    assert fwd_paged(lib, Tq=0, mq=0) == 0
