@@ -158,6 +158,29 @@ fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                           fa_dtype dtype, float scale, int num_splits, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/*
+ * fa_kv_append - write the K/V rows of new tokens into the paged cache.
+ * ("I/O-Aware Kernels", section "FlashInfer: I/O-aware attention for
+ * serving": paged KV layouts; the step that fills the pages fa_fwd_paged and
+ * fa_decode_paged read.)
+ *   k_new, v_new  [T_new, Hkv, d] dtype; sequence s owns rows
+ *                 cu_new[s] .. cu_new[s+1]-1 (device int32 [B+1], cu_new[0] = 0,
+ *                 non-decreasing, cu_new[B] = T_new; sequences may get none)
+ *   k_pool, v_pool [num_pages, page_size, Hkv, d] dtype (written in place)
+ *   page_table    device int32 [B, max_pages], as for fa_decode_paged
+ *   seq_lens_before device int32 [B]: tokens each sequence already holds
+ * Token i of sequence s goes to position p = seq_lens_before[s] + i, i.e.
+ * page page_table[s][p / 16], slot p % 16; nothing else in the pools changes
+ * (bit-exact copy). The caller owns seq_lens and adds the new counts
+ * afterwards. A token whose position is at or past max_pages * 16, or whose
+ * page-table entry is outside [0, num_pages), is not written. Any dtype; d
+ * must be 64 or 128, page_size 16. T_new = 0 is a no-op.
+ */
+fa_status fa_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                       const int32_t* cu_new, const int32_t* page_table,
+                       const int32_t* seq_lens_before, int B, int T_new, int max_pages,
+                       int num_pages, int page_size, int Hkv, int d, fa_dtype dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

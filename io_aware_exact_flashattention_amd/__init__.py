@@ -142,6 +142,34 @@ def fwd_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     return o, l
 
 
+def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
+              v_pool: torch.Tensor, cu_new: torch.Tensor, page_table: torch.Tensor,
+              seq_lens_before: torch.Tensor) -> None:
+    """Write new tokens' K/V rows ([T_new, Hkv, d], packed by cu_new int32
+    [B+1]) into the pools after the seq_lens_before tokens each sequence
+    holds. The pools are updated in place; seq_lens is the caller's."""
+    lib = _lib.load()
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("k_pool", k_pool), ("v_pool", v_pool),
+                 ("cu_new", cu_new), ("page_table", page_table),
+                 ("seq_lens_before", seq_lens_before)):
+        _dev_tensor(t, n)
+    _need(k_new.dim() == 3 and k_new.shape == v_new.shape and k_pool.dim() == 4
+          and k_pool.shape == v_pool.shape, "bad shapes")
+    _need(k_new.dtype == v_new.dtype == k_pool.dtype == v_pool.dtype, "tensors must share a dtype")
+    _need(cu_new.dtype == page_table.dtype == seq_lens_before.dtype == torch.int32,
+          "indices must be int32")
+    T_new, Hkv, d = k_new.shape
+    num_pages, page_size, Hkv_p, d_p = k_pool.shape
+    _need(Hkv_p == Hkv and d_p == d, "pool row shape differs from the new rows")
+    B = cu_new.shape[0] - 1
+    _need(page_table.dim() == 2 and page_table.shape[0] == B and seq_lens_before.shape == (B,),
+          "bad index shapes")
+    _lib.check(lib.fa_kv_append(k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
+                                v_pool.data_ptr(), cu_new.data_ptr(), page_table.data_ptr(),
+                                seq_lens_before.data_ptr(), B, T_new, page_table.shape[1],
+                                num_pages, page_size, Hkv, d, _dtype(k_new), _stream(k_new)))
+
+
 def decode_workspace_size(B: int, Hq: int, d: int, max_pages: int, page_size: int = 16,
                           num_splits: int = 0) -> int:
     return int(_lib.load().fa_decode_paged_workspace_size(B, Hq, d, max_pages, page_size,

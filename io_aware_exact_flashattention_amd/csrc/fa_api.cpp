@@ -189,4 +189,28 @@ fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                       const int32_t* cu_new, const int32_t* page_table,
+                       const int32_t* seq_lens_before, int B, int T_new, int max_pages,
+                       int num_pages, int page_size, int Hkv, int d, fa_dtype dtype, void* stream) {
+  if (!k_new || !v_new || !k_pool || !v_pool || !cu_new || !page_table || !seq_lens_before)
+    return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || T_new < 0 || max_pages <= 0 || num_pages <= 0 || page_size <= 0 || Hkv <= 0 ||
+      d <= 0)
+    return FA_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return FA_ERR_INVALID_ARG;
+  if (page_size != kPageSize) return FA_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d)) return FA_ERR_UNSUPPORTED;
+  if (T_new == 0) return FA_OK;
+  fa::AppendParams p{};
+  p.k_new = k_new; p.v_new = v_new; p.k_pool = k_pool; p.v_pool = v_pool;
+  p.cu_new = cu_new; p.page_table = page_table; p.seq_lens_before = seq_lens_before;
+  p.B = B; p.max_pages = max_pages; p.num_pages = num_pages;
+  p.row_bytes = (int64_t)Hkv * d * (dtype == FA_F32 ? 4 : 2);
+  hipError_t e = fa::launch_append(p, T_new, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // extern "C"

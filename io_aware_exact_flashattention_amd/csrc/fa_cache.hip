@@ -1,0 +1,54 @@
+// fa_cache.hip - appending new tokens' K/V rows to the paged cache, gfx950.
+//
+// The paged KV layout of the page "I/O-Aware Kernels" (datasystem.school,
+// Module 5), section "FlashInfer: I/O-aware attention for serving": a pool of
+// 16-token pages and a page table per sequence. Appending n tokens to a
+// sequence that holds L writes token i to position L + i: page
+// page_table[s][(L+i) / 16], slot (L+i) % 16. The kernel moves bits only.
+//
+// One workgroup per new token (grid x) and per tensor (grid y: 0 = K, 1 = V);
+// its threads copy the token row (Hkv * d values, a multiple of 16 bytes) in
+// 16-byte pieces. This is a pure HBM copy: 2 x row bytes read and written
+// per token and tensor.
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kAppendThreads = 256;
+
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) {
+  const int t = blockIdx.x;  // token of the batch
+  const bool is_v = blockIdx.y != 0;
+  // its sequence: cu_new[s] <= t < cu_new[s+1] (cu_new non-decreasing, cu_new[0] = 0,
+  // cu_new[B] = T_new > t)
+  int lo = 0, hi = p.B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.cu_new[mid] <= t) lo = mid;
+    else hi = mid;
+  }
+  const int s = lo;
+  const int64_t pos = (int64_t)p.seq_lens_before[s] + (t - p.cu_new[s]);
+  // a position outside the sequence's page-table row, or a page outside the
+  // pool, is not written
+  if (pos < 0 || pos >= (int64_t)p.max_pages * kPageRows) return;
+  const int page = p.page_table[(int64_t)s * p.max_pages + (pos / kPageRows)];
+  if (page < 0 || page >= p.num_pages) return;
+  const int64_t row = (int64_t)page * kPageRows + (pos % kPageRows);
+  const char* src = (const char*)(is_v ? p.v_new : p.k_new) + (int64_t)t * p.row_bytes;
+  char* dst = (char*)(is_v ? p.v_pool : p.k_pool) + row * p.row_bytes;
+  const int chunks = (int)(p.row_bytes / 16);
+  for (int c = threadIdx.x; c < chunks; c += kAppendThreads)
+    ((uint4*)dst)[c] = ((const uint4*)src)[c];
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, int T_new, hipStream_t st) {
+  hipLaunchKernelGGL(append_kernel, dim3(T_new, 2), dim3(kAppendThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace fa

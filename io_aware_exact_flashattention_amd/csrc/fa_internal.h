@@ -53,6 +53,20 @@ struct DecodeParams {
   float scale_log2;
 };
 
+// Appending new tokens to the paged cache.
+constexpr int kPageRows = 16;  // token slots per page
+struct AppendParams {
+  const void* k_new;             // [T_new, Hkv, d]
+  const void* v_new;
+  void* k_pool;                  // [num_pages, 16, Hkv, d]
+  void* v_pool;
+  const int32_t* cu_new;         // [B+1]
+  const int32_t* page_table;     // [B, max_pages]
+  const int32_t* seq_lens_before;  // [B]
+  int B, max_pages, num_pages;
+  int64_t row_bytes;             // Hkv * d * element size (a multiple of 16)
+};
+
 enum class Dt { F32, F16, Bf16 };
 
 // Each launcher enqueues its kernel(s) on `stream` and returns hipGetLastError().
@@ -64,5 +78,7 @@ hipError_t launch_fwd_paged(const FwdParams& p, Dt dt, int d, bool causal, int g
                             hipStream_t stream);
 
 hipError_t launch_decode(const DecodeParams& p, Dt dt, int d, hipStream_t stream);
+
+hipError_t launch_append(const AppendParams& p, int T_new, hipStream_t stream);
 
 }  // namespace fa

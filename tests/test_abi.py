@@ -133,3 +133,24 @@ def test_fwd_paged_rejects(lib, kw, expect):
 
 def test_fwd_paged_empty_is_noop(lib):
     assert fwd_paged(lib, Tq=0, mq=0) == 0
+
+
+def kv_append(lib, **kw):
+    a = dict(kn=P, vn=P, kp=P, vp=P, cu=P, pt=P, lb=P, B=2, T=4, mp=4, npg=8, ps=16, Hkv=2, d=128,
+             dt=2, stream=None)
+    a.update(kw)
+    return lib.fa_kv_append(a["kn"], a["vn"], a["kp"], a["vp"], a["cu"], a["pt"], a["lb"], a["B"],
+                            a["T"], a["mp"], a["npg"], a["ps"], a["Hkv"], a["d"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(kn=None), 1), (dict(vp=None), 1), (dict(cu=None), 1), (dict(pt=None), 1), (dict(lb=None), 1),
+    (dict(B=0), 1), (dict(T=-1), 1), (dict(mp=0), 1), (dict(npg=0), 1), (dict(Hkv=0), 1),
+    (dict(dt=5), 1), (dict(kp=24), 1), (dict(ps=32), 2), (dict(d=80), 2),
+])
+def test_kv_append_rejects(lib, kw, expect):
+    assert kv_append(lib, **kw) == expect
+
+
+def test_kv_append_empty_is_noop(lib):
+    assert kv_append(lib, T=0) == 0
