@@ -303,6 +303,41 @@ def paged_prefill(lens_q, lens_k, Hq, Hkv, d, dtype, seed, permute=True, tail_fi
     return PagedPrefill(q, cu_q, kv)
 
 
+@dataclass
+class Cascade:
+    """Decode inputs for sequences that share a cached prefix: one pool holds
+    the prefix pages and every sequence's own pages."""
+    q: np.ndarray              # [B, Hq, d]
+    pool: Paged                # row 0 of its page table: the prefix; rows 1..B: suffixes
+    prefix_len: int
+
+    @property
+    def prefix_pages(self):
+        return self.pool.page_table[0, :(self.prefix_len + PAGE_SIZE - 1) // PAGE_SIZE]
+
+    @property
+    def page_table(self):
+        return np.ascontiguousarray(self.pool.page_table[1:])
+
+    @property
+    def seq_lens(self):
+        return self.pool.seq_lens[1:]
+
+    def keys(self, b, which="k"):
+        """Contiguous keys (or values) of sequence b: prefix then suffix."""
+        src = self.pool.k_seq if which == "k" else self.pool.v_seq
+        cu = self.pool.cu_k
+        return np.concatenate([src[cu[0]:cu[1]], src[cu[b + 1]:cu[b + 2]]])
+
+
+def cascade(prefix_len, suffix_lens, Hq, Hkv, d, dtype, seed, permute=True, tail_fill="zero",
+            name="") -> Cascade:
+    lens = np.concatenate([[prefix_len], np.asarray(suffix_lens, dtype=np.int64)])
+    pool = paged(lens, Hq, Hkv, d, dtype, seed, permute=permute, tail_fill=tail_fill, name=name)
+    q = _draw_q(seed + 1000, (len(lens) - 1, Hq, d), dtype)
+    return Cascade(q, pool, int(prefix_len))
+
+
 def chunked_prefill_lengths(seed=5, B=16):
     """A chunked-prefill batch: cached prefixes U[0, 8192] and chunks U[1, 2048]
     tokens (keys = prefix + chunk)."""

@@ -159,6 +159,46 @@ fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                           size_t workspace_bytes, void* stream);
 
 /*
+ * fa_decode_cascade_workspace_size - bytes of device workspace that
+ * fa_decode_cascade needs (float32 partials of the prefix splits and of the
+ * suffix splits). Returns 0 for invalid sizes.
+ */
+size_t fa_decode_cascade_workspace_size(int B, int Hq, int d, int prefix_len, int max_pages,
+                                        int page_size);
+
+/*
+ * fa_decode_cascade - decode of B sequences that share one cached prefix.
+ * ("I/O-Aware Kernels", section "FlashInfer: I/O-aware attention for
+ * serving": paged KV layouts, grouped-query attention, and the shared
+ * prefixes of the RadixAttention layout seen from the kernel.)
+ * The keys of sequence b are the prefix_len tokens held on prefix_pages
+ * followed by its own seq_lens[b] tokens held through page_table row b; its
+ * one query sees all of them. The prefix pages are read once for the whole
+ * batch: one pass reduces them against the queries of every sequence (the
+ * query heads of a KV head as columns of one MFMA operand), a second pass
+ * reduces each sequence's own pages, and a log-sum-exp merge combines both.
+ *   q [B, Hq, d], o [B, Hq, d] dtype; lse [B, Hq] float32
+ *   k_pool, v_pool [num_pages, page_size, Hkv, d] dtype (prefix and
+ *              suffix pages live in the same pools)
+ *   prefix_pages device int32 [ceil(prefix_len / 16)]: physical pages of
+ *              prefix tokens 16*i .. 16*i+15 (slots of a last, partial prefix
+ *              page beyond prefix_len are not read); may be NULL when
+ *              prefix_len == 0
+ *   page_table device int32 [B, max_pages], seq_lens device int32 [B]: the
+ *              suffix of each sequence, as for fa_decode_paged (suffix
+ *              token 0 is key prefix_len); seq_lens[b] may be 0
+ *   workspace  at least fa_decode_cascade_workspace_size(...) bytes of
+ *              device memory owned by the caller (scratch).
+ * page_size must be 16, dtype FA_F16 or FA_BF16. Splits of 32 pages.
+ */
+fa_status fa_decode_cascade(const void* q, const void* k_pool, const void* v_pool, void* o,
+                            float* lse, const int32_t* prefix_pages, int prefix_len,
+                            const int32_t* page_table, const int32_t* seq_lens, int B,
+                            int max_pages, int num_pages, int page_size, int Hq, int Hkv, int d,
+                            fa_dtype dtype, float scale, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * fa_kv_append - write the K/V rows of new tokens into the paged cache.
  * ("I/O-Aware Kernels", section "FlashInfer: I/O-aware attention for
  * serving": paged KV layouts; the step that fills the pages fa_fwd_paged and

@@ -142,6 +142,46 @@ def fwd_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     return o, l
 
 
+def decode_cascade(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                   prefix_pages: torch.Tensor | None, prefix_len: int, page_table: torch.Tensor,
+                   seq_lens: torch.Tensor, scale: float | None = None,
+                   workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                   lse: torch.Tensor | None = None):
+    """Decode of sequences sharing one prefix: q [B, Hq, d]; prefix_pages
+    int32 [ceil(prefix_len/16)]; page_table int32 [B, max_pages] and seq_lens
+    int32 [B] describe each sequence's own suffix -> (O like q, LSE [B, Hq])."""
+    lib = _lib.load()
+    for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("page_table", page_table),
+                 ("seq_lens", seq_lens)):
+        _dev_tensor(t, n)
+    if prefix_len > 0:
+        _dev_tensor(prefix_pages, "prefix_pages")
+        _need(prefix_pages.dtype == torch.int32, "prefix_pages must be int32")
+    _need(q.dim() == 3 and k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "bad shapes")
+    _need(q.dtype == k_pool.dtype == v_pool.dtype, "q and pools must share a dtype")
+    _need(page_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "indices must be int32")
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv, _ = k_pool.shape
+    max_pages = page_table.shape[1]
+    _need(page_table.shape[0] == B and seq_lens.shape == (B,), "bad index shapes")
+    if scale is None:
+        scale = default_scale(d)
+    need = int(lib.fa_decode_cascade_workspace_size(B, Hq, d, int(prefix_len), max_pages,
+                                                    page_size))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    pp = prefix_pages.data_ptr() if (prefix_pages is not None and prefix_len > 0) else None
+    _lib.check(lib.fa_decode_cascade(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                     o.data_ptr(), l.data_ptr(), pp, int(prefix_len),
+                                     page_table.data_ptr(), seq_lens.data_ptr(), B, max_pages,
+                                     num_pages, page_size, Hq, Hkv, d, _dtype(q), float(scale),
+                                     workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream(q)))
+    return o, l
+
+
 def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
               v_pool: torch.Tensor, cu_new: torch.Tensor, page_table: torch.Tensor,
               seq_lens_before: torch.Tensor) -> None:

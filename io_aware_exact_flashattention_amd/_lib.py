@@ -15,7 +15,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 
 EXPORTS = ("fa_status_string", "fa_version", "fa_fwd", "fa_fwd_varlen", "fa_fwd_paged",
-           "fa_decode_paged_workspace_size", "fa_decode_paged", "fa_kv_append")
+           "fa_decode_paged_workspace_size", "fa_decode_paged", "fa_decode_cascade_workspace_size",
+           "fa_decode_cascade", "fa_kv_append")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
@@ -30,6 +31,11 @@ _SIGNATURES = {
     "fa_fwd_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                           _i, _i, _f, _i, _vp]),
     "fa_decode_paged_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "fa_decode_cascade_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    # q k_pool v_pool o lse prefix_pages prefix_len page_table seq_lens B max_pages num_pages
+    # page_size Hq Hkv d dtype scale workspace workspace_bytes stream
+    "fa_decode_cascade": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                               _i, _i, _f, _vp, _sz, _vp]),
     # k_new v_new k_pool v_pool cu_new page_table seq_lens_before B T_new max_pages num_pages
     # page_size Hkv d dtype stream
     "fa_kv_append": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),

@@ -189,6 +189,61 @@ fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Splits of a cascade decode: prefix splits (32 pages each) lead, then the
+// suffix splits of the longest suffix.
+static void cascade_splits(int prefix_len, int max_pages, int& s_pre, int& s_suf) {
+  const int pre_pages = (prefix_len + kPageSize - 1) / kPageSize;
+  s_pre = (pre_pages + kAutoPagesPerSplit - 1) / kAutoPagesPerSplit;
+  s_suf = (max_pages + kAutoPagesPerSplit - 1) / kAutoPagesPerSplit;
+}
+
+size_t fa_decode_cascade_workspace_size(int B, int Hq, int d, int prefix_len, int max_pages,
+                                        int page_size) {
+  if (B <= 0 || Hq <= 0 || d <= 0 || prefix_len < 0 || max_pages <= 0 || page_size <= 0) return 0;
+  int s_pre, s_suf;
+  cascade_splits(prefix_len, max_pages, s_pre, s_suf);
+  return (size_t)B * Hq * (size_t)(s_pre + s_suf) * ((size_t)d + 1) * sizeof(float);
+}
+
+fa_status fa_decode_cascade(const void* q, const void* k_pool, const void* v_pool, void* o,
+                            float* lse, const int32_t* prefix_pages, int prefix_len,
+                            const int32_t* page_table, const int32_t* seq_lens, int B,
+                            int max_pages, int num_pages, int page_size, int Hq, int Hkv, int d,
+                            fa_dtype dtype, float scale, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  fa_status st = check_common(q, k_pool, v_pool, o, lse, Hq, Hkv, d, dtype, scale);
+  if (st != FA_OK) return st;
+  if (!page_table || !seq_lens || !workspace) return FA_ERR_INVALID_ARG;
+  if (prefix_len < 0 || (prefix_len > 0 && !prefix_pages)) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || max_pages <= 0 || num_pages <= 0 || page_size <= 0) return FA_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  if (page_size != kPageSize) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_decode_cascade_workspace_size(B, Hq, d, prefix_len, max_pages, page_size);
+  if (need == 0 || workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  int s_pre, s_suf;
+  cascade_splits(prefix_len, max_pages, s_pre, s_suf);
+  if (B > 65535) return FA_ERR_UNSUPPORTED;  // grid y of the split merge
+  if ((int64_t)B * (s_pre + s_suf) * Hq > INT32_MAX) return FA_ERR_UNSUPPORTED;
+
+  fa::DecodeParams p{};
+  p.q = q; p.k_pool = k_pool; p.v_pool = v_pool; p.o = o; p.lse = lse;
+  p.page_table = page_table; p.seq_lens = seq_lens;
+  p.B = B; p.max_pages = max_pages; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.pages_per_split = kAutoPagesPerSplit;
+  p.max_splits = s_pre + s_suf;
+  p.scale_log2 = scale * kLog2e;
+  p.prefix_pages = prefix_pages;
+  p.prefix_len = prefix_len;
+  p.prefix_splits = s_pre;
+  p.split_offset = s_pre;
+  float* ws = static_cast<float*>(workspace);
+  p.o_part = ws;
+  p.lse_part = ws + (size_t)B * Hq * p.max_splits * d;
+  hipError_t e = fa::launch_decode_cascade(p, to_dt(dtype), d, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                        const int32_t* cu_new, const int32_t* page_table,
                        const int32_t* seq_lens_before, int B, int T_new, int max_pages,

@@ -107,7 +107,11 @@ __device__ __forceinline__ void settle(int& x) { asm volatile("" : "+v"(x)); }
 // the widest head block needs more registers and runs four.
 template <int D, int GB> constexpr int decode_waves_per_simd() { return D * GB > 512 ? 4 : 5; }
 
-template <typename T, int D, int GB>
+// PREFIX: the shared-prefix pass of a cascade decode. A work item is then
+// (block of 16 query columns, prefix split, KV head); column c of block qb is
+// query r = 16 qb + c of the r-th (sequence, head-in-group) pair of the KV
+// head, so the prefix pages are read once for every query of the group.
+template <typename T, int D, int GB, bool PREFIX = false>
 __global__ __launch_bounds__(64 * kWavesPerBlock)
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode_split_kernel(
     DecodeParams p) {
@@ -126,19 +130,45 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
   static_assert(KSTEP * 1024 == KBYTES && VI * 1024 == KBYTES, "page layout");
   __shared__ uint4 lds[kWavesPerBlock][kWaveLds / 16];
 
-  // work item: (sequence, split, KV head, head block), head block fastest
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int nhb = p.group / GB;
-  const int nh = p.Hkv * nhb;
   int item = blockIdx.x * kWavesPerBlock + wave;
-  const int hb = item % nh;
-  item /= nh;
-  const int s = item % p.max_splits;
-  const int b = item / p.max_splits;
-  if (b >= p.B) return;
-  const int g = hb / nhb;
-  const int h0 = g * p.group + (hb % nhb) * GB;
-  const int L = p.seq_lens[b];
+  int b, g, h0, s, L, qb = 0;
+  const int32_t* pt;
+  if (PREFIX) {
+    // work item: (query block, prefix split, KV head), KV head fastest
+    g = item % p.Hkv;
+    item /= p.Hkv;
+    s = item % p.prefix_splits;
+    qb = item / p.prefix_splits;
+    if (qb * GB >= p.B * p.group) return;
+    b = 0;
+    h0 = 0;
+    L = p.prefix_len;
+    pt = p.prefix_pages;
+  } else {
+    // work item: (sequence, split, KV head, head block), head block fastest
+    const int nhb = p.group / GB;
+    const int nh = p.Hkv * nhb;
+    const int nsplit = p.max_splits - p.split_offset;  // splits of this pass
+    const int hb = item % nh;
+    item /= nh;
+    s = item % nsplit;
+    b = item / nsplit;
+    if (b >= p.B) return;
+    g = hb / nhb;
+    h0 = g * p.group + (hb % nhb) * GB;
+    L = p.seq_lens[b];
+    pt = p.page_table + (int64_t)b * p.max_pages;
+  }
+  // query row (sequence * Hq + head) of column c
+  auto q_row_of = [&](int c) -> int64_t {
+    if (PREFIX) {
+      const int r = qb * GB + c;
+      return (int64_t)(r / p.group) * p.Hq + g * p.group + r % p.group;
+    }
+    return (int64_t)b * p.Hq + h0 + c;
+  };
+  auto column_valid = [&](int c) { return !PREFIX || qb * GB + c < p.B * p.group; };
   const int npages = (L + kPage - 1) / kPage;
   const int pg0 = s * p.pages_per_split;
   if (pg0 >= npages) return;
@@ -148,18 +178,17 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
   const int l16 = lane & 15, j = lane >> 4;  // score layout
   const float c2 = p.scale_log2;
 
-  // B operand: Q^T, heads h0 .. h0+GB-1 in columns 0..GB-1
+  // B operand: Q^T, columns 0..GB-1 (zero for absent queries)
   uint4 qf[KSTEP];
 #pragma unroll
   for (int st = 0; st < KSTEP; ++st) qf[st] = make_uint4(0, 0, 0, 0);
-  if (l16 < GB) {
-    const uint16_t* src = (const uint16_t*)p.q + ((int64_t)b * p.Hq + h0 + l16) * D + j * DL;
+  if (l16 < GB && column_valid(l16)) {
+    const uint16_t* src = (const uint16_t*)p.q + q_row_of(l16) * D + j * DL;
 #pragma unroll
     for (int st = 0; st < KSTEP; ++st) qf[st] = *(const uint4*)(src + 8 * st);
   }
   // Page indices of the split (at most 64 pages): lane i holds entry
   // pg0 + i; each page's index is read from its lane.
-  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
   int pg_idx = pg0 + lane < pg1 ? pt[pg0 + lane] : 0;
 #pragma unroll
   for (int st = 0; st < KSTEP; ++st) settle(qf[st]);
@@ -290,7 +319,8 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
 #pragma unroll
   for (int h = 0; h < GB; ++h) {
     const float lt = lane_value(l_lane, h);
-    const int64_t row = ((int64_t)b * p.Hq + h0 + h) * p.max_splits + s;
+    if (!column_valid(h)) continue;
+    const int64_t row = q_row_of(h) * p.max_splits + (PREFIX ? 0 : p.split_offset) + s;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     float* dst = p.o_part + row * D + lane * VPL;
     if constexpr (VPL == 2) *(float2*)dst = make_float2(o[h][0] * inv, o[h][1] * inv);
@@ -318,7 +348,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
   const int sg = tid >> 5, q = tid & 31;
   const int L = p.seq_lens[b];
   const int npages = (L + kPage - 1) / kPage;
-  const int ns = (npages + p.pages_per_split - 1) / p.pages_per_split;
+  const int ns = p.prefix_splits + (npages + p.pages_per_split - 1) / p.pages_per_split;
   const int64_t row = ((int64_t)b * p.Hq + h) * p.max_splits;
   const float* lp = p.lse_part + row;
   const float* op = p.o_part + row * D + q * PER;
@@ -374,7 +404,16 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
 
 template <typename T, int D, int GB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t st) {
-  const int64_t items = (int64_t)p.B * p.max_splits * p.Hkv * (p.group / GB);
+  if (p.prefix_len > 0) {
+    constexpr int QB = 16;
+    const int64_t items = (int64_t)((p.B * p.group + QB - 1) / QB) * p.prefix_splits * p.Hkv;
+    const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
+    hipLaunchKernelGGL((decode_split_kernel<T, D, QB, true>), dim3(blocks),
+                       dim3(64 * kWavesPerBlock), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t items = (int64_t)p.B * (p.max_splits - p.split_offset) * p.Hkv * (p.group / GB);
   const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
   hipLaunchKernelGGL((decode_split_kernel<T, D, GB>), dim3(blocks), dim3(64 * kWavesPerBlock), 0,
                      st, p);
@@ -394,6 +433,11 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+// launch_t runs the prefix pass whenever p.prefix_len > 0.
+hipError_t launch_decode_cascade(const DecodeParams& p, Dt dt, int d, hipStream_t st) {
+  return launch_decode(p, dt, d, st);
+}
 
 hipError_t launch_decode(const DecodeParams& p, Dt dt, int d, hipStream_t st) {
   switch (dt) {

@@ -51,6 +51,15 @@ struct DecodeParams {
   int pages_per_split;
   int max_splits;
   float scale_log2;
+  // Shared-prefix (cascade) decode: every sequence's keys are the prefix_len
+  // tokens on prefix_pages followed by its own seq_lens[b] tokens. The prefix
+  // is reduced once for all queries into splits [0, prefix_splits); the
+  // split kernel writes its splits from split_offset on. All zero/null for
+  // a plain decode.
+  const int32_t* prefix_pages;
+  int prefix_len;
+  int prefix_splits;
+  int split_offset;
 };
 
 // Appending new tokens to the paged cache.
@@ -78,6 +87,8 @@ hipError_t launch_fwd_paged(const FwdParams& p, Dt dt, int d, bool causal, int g
                             hipStream_t stream);
 
 hipError_t launch_decode(const DecodeParams& p, Dt dt, int d, hipStream_t stream);
+// Cascade decode: prefix pass (when p.prefix_len > 0), suffix pass, merge.
+hipError_t launch_decode_cascade(const DecodeParams& p, Dt dt, int d, hipStream_t stream);
 
 hipError_t launch_append(const AppendParams& p, int T_new, hipStream_t stream);
 

@@ -154,3 +154,29 @@ def test_kv_append_rejects(lib, kw, expect):
 
 def test_kv_append_empty_is_noop(lib):
     assert kv_append(lib, T=0) == 0
+
+
+def cascade(lib, **kw):
+    a = dict(q=P, kp=P, vp=P, o=P, lse=P, pp=P, pl=100, pt=P, sl=P, B=2, mp=4, npg=8, ps=16, Hq=4,
+             Hkv=1, d=128, dt=2, scale=0.1, ws=P, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.fa_decode_cascade(a["q"], a["kp"], a["vp"], a["o"], a["lse"], a["pp"], a["pl"], a["pt"],
+                                 a["sl"], a["B"], a["mp"], a["npg"], a["ps"], a["Hq"], a["Hkv"], a["d"],
+                                 a["dt"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(pp=None), 1), (dict(pl=-1), 1), (dict(pt=None), 1), (dict(ws=None), 1), (dict(wsb=16), 1),
+    (dict(B=0), 1), (dict(mp=0), 1), (dict(ps=8), 2), (dict(dt=0), 2), (dict(d=80), 2),
+])
+def test_cascade_rejects(lib, kw, expect):
+    assert cascade(lib, **kw) == expect
+
+
+def test_cascade_workspace_size(lib):
+    f = lib.fa_decode_cascade_workspace_size
+    # prefix 100 tokens = 7 pages -> 1 split; suffix 4 pages -> 1 split
+    assert f(2, 4, 128, 100, 4, 16) == 2 * 4 * 2 * 129 * 4
+    assert f(2, 4, 128, 0, 4, 16) == 2 * 4 * 1 * 129 * 4
+    assert f(1, 1, 64, 16384, 70, 16) == 1 * 1 * (32 + 3) * 65 * 4
+    assert f(0, 4, 128, 1, 4, 16) == 0
