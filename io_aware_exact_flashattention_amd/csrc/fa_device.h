@@ -65,6 +65,30 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 // Lane value exchange within a wavefront (64 lanes).
 __device__ __forceinline__ float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// The values of lanes i and i^32, both in every lane: v_permlane32_swap
+// exchanges the two 32-lane halves inside the vector ALU, with no LDS round
+// trip (a ds_bpermute would queue behind the LDS reads of other waves).
+// After the swap, lanes below 32 hold (x[i], x[i+32]) and lanes from 32 on
+// hold (x[i-32], x[i]).
+__device__ __forceinline__ void half_pair(float x, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];  // copy out before the bit cast
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+// max / sum of lanes i and i^32 (the same value in both lanes of a pair)
+__device__ __forceinline__ float max_halves(float x) {
+  float a, b;
+  half_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float a, b;
+  half_pair(x, a, b);
+  return a + b;
+}
+
 // Byte-select of two 32-bit words (v_perm_b32): result byte i is byte
 // sel[i] of the 8-byte value (hi:lo).
 __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
@@ -86,6 +110,15 @@ __device__ __forceinline__ void load_to_lds(const void* gsrc, uint32_t lds_wave_
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gsrc), "s"(lds_wave_base)
+               : "memory", "m0");
+}
+
+// The same copy from a wave-uniform base (an SGPR pair) plus a 32-bit
+// per-lane byte offset: no 64-bit address arithmetic per lane.
+__device__ __forceinline__ void load_to_lds_sv(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_wave_base)
                : "memory", "m0");
 }
 

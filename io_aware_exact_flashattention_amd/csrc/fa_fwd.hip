@@ -212,15 +212,24 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
 
   // ---- direct-to-LDS tile loads: this lane's rows and source chunks ----
   // Load n of thread tid fills LDS bytes (n*kThreads + tid)*16 of a tile;
-  // the swizzle is applied on the source side.
-  int ld_row[LD], k_col[LD], v_col[LD];
-#pragma unroll
-  for (int n = 0; n < LD; ++n) {
+  // the swizzle is applied on the source side: tile row ld_row(n), source
+  // element column ld_col(n).
+  auto ld_row = [&](int n) { return (n * kThreads + tid) * 16 / G::ROWB; };
+  auto ld_col = [&](int n, bool k_side) {
     const int pos = (n * kThreads + tid) * 16;
     const int r = pos / G::ROWB, pc = (pos % G::ROWB) / 16;
-    ld_row[n] = r;
-    k_col[n] = 8 * (pc ^ G::k_swz(r));
-    v_col[n] = 8 * (pc ^ G::v_swz(r));
+    return 8 * (pc ^ (k_side ? G::k_swz(r) : G::v_swz(r)));
+  };
+  // The same loads as byte offsets from the tile's first row, for tiles
+  // whose rows all lie inside the sequence (every tile but a ragged last
+  // one): the tile base is then wave-uniform and the per-lane address
+  // needs no 64-bit arithmetic. Needs kv_row * kBN * 2 bytes < 2^31.
+  const bool uniform_rows = !PAGED && p.kv_row < (1 << 24);
+  uint32_t k_voff[LD], v_voff[LD];
+#pragma unroll
+  for (int n = 0; n < LD; ++n) {
+    k_voff[n] = 2u * (uint32_t)(ld_row(n) * p.kv_row + ld_col(n, true));
+    v_voff[n] = 2u * (uint32_t)(ld_row(n) * p.kv_row + ld_col(n, false));
   }
   const uint16_t* kbase = (const uint16_t*)p.k + (int64_t)k0 * p.kv_row + (int64_t)g * D;
   const uint16_t* vbase = (const uint16_t*)p.v + (int64_t)k0 * p.kv_row + (int64_t)g * D;
@@ -247,20 +256,33 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
     return min(key, last_key);
   };
 
-  // Tiles past the last one are loaded too (rows clamped to the last key,
-  // into ring slots no longer read), so every step issues and awaits the
-  // same number of loads.
+  // Both paths issue LD loads per lane, so the wait counts below do not
+  // depend on which one a tile takes.
   auto issue_k = [&](int j) {
     const uint32_t st = lds_wave + (j % kKStages) * G::BYTES;
+    if (uniform_rows && (j + 1) * kBN <= Lk) {
+      const uint16_t* tb = kbase + (int64_t)j * kBN * p.kv_row;
 #pragma unroll
-    for (int n = 0; n < LD; ++n)
-      load_to_lds(kbase + key_row(j * kBN + ld_row[n]) * p.kv_row + k_col[n], st + n * kThreads * 16);
+      for (int n = 0; n < LD; ++n) load_to_lds_sv(tb, k_voff[n], st + n * kThreads * 16);
+    } else {
+#pragma unroll
+      for (int n = 0; n < LD; ++n)
+        load_to_lds(kbase + key_row(j * kBN + ld_row(n)) * p.kv_row + ld_col(n, true),
+                    st + n * kThreads * 16);
+    }
   };
   auto issue_v = [&](int j) {
     const uint32_t st = lds_wave + (kKStages + j % kVStages) * G::BYTES;
+    if (uniform_rows && (j + 1) * kBN <= Lk) {
+      const uint16_t* tb = vbase + (int64_t)j * kBN * p.kv_row;
 #pragma unroll
-    for (int n = 0; n < LD; ++n)
-      load_to_lds(vbase + key_row(j * kBN + ld_row[n]) * p.kv_row + v_col[n], st + n * kThreads * 16);
+      for (int n = 0; n < LD; ++n) load_to_lds_sv(tb, v_voff[n], st + n * kThreads * 16);
+    } else {
+#pragma unroll
+      for (int n = 0; n < LD; ++n)
+        load_to_lds(vbase + key_row(j * kBN + ld_row(n)) * p.kv_row + ld_col(n, false),
+                    st + n * kThreads * 16);
+    }
   };
   // Slot byte offsets inside the LDS array (K ring, then V ring). Passed
   // through readfirstlane so that loop strength reduction does not turn
@@ -332,8 +354,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   // computes its softmax.
   //   slot 2j:   group 0 softmax(j),  group 1 matrix(j-1) (scores of tile 0 for j = 0)
   //   slot 2j+1: group 0 matrix(j),   group 1 softmax(j)
-  // Loads: the barrier opening slot 2j+1 waits for K tile j+1 and V tile j
-  // (issued two slots earlier) and issues K tile j+2 and V tile j+1.
+  // Loads: the barrier opening slot 2j issues K tile j+2; the one opening
+  // slot 2j+1 waits for K tile j+1 and V tile j and issues V tile j+1, so
+  // each slot carries half of the load issue.
   const int grp = wave >> 2;
   f32x16 sc[NB];   // scores of the tile being worked on
   uint4 pf[NB][2]; // its probabilities, B operand of O^T += V^T P^T
@@ -392,12 +415,18 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
         for (int r = 0; r < 16; ++r)
           if (32 * kb + 8 * (r >> 2) + (r & 3) > t) sc[kb][r] = neg_inf();
     }
-    float mx = neg_inf();
+    // row max: one chain per score block, then across the lane halves
+    float mk[NB];
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
+    for (int kb = 0; kb < NB; ++kb) {
+      mk[kb] = sc[kb][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    mx = fmaxf(mx, xor_lane(mx, 32));
+      for (int r = 1; r < 16; ++r) mk[kb] = fmaxf(mk[kb], sc[kb][r]);
+    }
+    float mx = mk[0];
+#pragma unroll
+    for (int kb = 1; kb < NB; ++kb) mx = fmaxf(mx, mk[kb]);
+    mx = max_halves(mx);
     const float mx2 = mx * c2;  // -inf when the row sees no key of this tile
     const bool raise = mx2 > m_run + kRescale;
     const float alpha = fast_exp2(raise ? m_run - mx2 : 0.f);  // exp2(0) = 1
@@ -409,7 +438,8 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
     }
-    float rs = 0.f;
+    // row sum (fp32, before rounding): four independent partial sums
+    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -418,12 +448,12 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           e[i] = fast_exp2(fmaf(sc[kb][8 * u + i], c2, -base));
-          rs += e[i];
+          rs4[i & 3] += e[i];
         }
         pf[kb][u] = make_uint4(E::pack2(e[0], e[1]), E::pack2(e[2], e[3]),
                                E::pack2(e[4], e[5]), E::pack2(e[6], e[7]));
       }
-    l_run = l_run * alpha + rs;
+    l_run = l_run * alpha + ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3]));
     // probabilities complete before the barrier that ends the phase (the
     // compiler may not sink this arithmetic into the matrix phase)
 #pragma unroll
@@ -455,37 +485,49 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   __syncthreads();
   if (grp == 0) scores0();
 
-  // Barrier opening slot 2j+1: K tile j+1 and V tile j (issued two slots
-  // earlier) have landed for every wave, and the slots that K tile j+2 and
-  // V tile j+1 go to were last read in slot 2j-2.
-  auto odd_barrier = [&](int j) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (j + 2 < n_kv) issue_k(j + 2);
-    if (j + 1 < n_kv) issue_v(j + 1);
+  // Barrier k opens slot k. In issue order the loads are K tile m+1 (at
+  // barrier 2m-2, the prologue for m = 0), V tile m (barrier 2m-1, the
+  // prologue for m = 0), K tile m+2 (barrier 2m).
+  // Barrier 2m+1 waits for K tile m+1 and V tile m, read by the matrix
+  // phases of slots 2m+1 and 2m+2; only K tile m+2 may still be in flight.
+  // It then issues V tile m+1 into the slot of V tile m-2, last read in
+  // slot 2m-2. Barrier 2m waits for nothing (slot 2m reads tiles that
+  // barrier 2m-1 awaited) and issues K tile m+2 into the slot of K tile
+  // m-1, last read in slot 2m-2.
+  auto barrier = [&](int k) {
+    const int m = k >> 1;
+    if ((k & 1) == 0) {
+      __syncthreads();
+      if (m + 2 < n_kv) issue_k(m + 2);
+    } else {
+      if (m + 2 < n_kv) __builtin_amdgcn_s_waitcnt(wait_vmcnt(LD));
+      else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      if (m + 1 < n_kv) issue_v(m + 1);
+    }
   };
-  // Each group runs its own loop; both pass 2 n_kv + 1 barriers.
+  // Each group runs its own loop; both pass barriers 0 .. 2 n_kv in order.
   if (grp == 0) {
-    __syncthreads();  // slot 0
+    barrier(0);
     for (int j = 0; j < n_kv; ++j) {
       softmax(j);     // slot 2j
-      odd_barrier(j);
+      barrier(2 * j + 1);
       matrix(j);      // slot 2j+1
-      __syncthreads();
+      barrier(2 * j + 2);
     }
   } else {
-    __syncthreads();  // slot 0
-    scores0();
+    barrier(0);
+    scores0();        // slot 0
     for (int j = 0; j < n_kv; ++j) {
-      odd_barrier(j);
+      barrier(2 * j + 1);
       softmax(j);     // slot 2j+1
-      __syncthreads();
+      barrier(2 * j + 2);
       matrix(j);      // slot 2j+2
     }
   }
 
   // ---- epilogue: O = O / l, LSE = ln(sum exp) ----
-  const float l_tot = l_run + xor_lane(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   if (my_row < Lq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* dst = (uint16_t*)p.o + (int64_t)(q0 + my_row) * p.q_row + (int64_t)w.h * D;
