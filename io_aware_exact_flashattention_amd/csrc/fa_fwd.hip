@@ -22,8 +22,8 @@
 //    round-to-nearest conversion to 16 bits, without leaving the lane. The
 //    V^T operand is read from the row-major V tile with ds_read_b64_tr_b16.
 //  * K and V tiles reach LDS by direct-to-LDS global loads (no register
-//    round trip) into two 3-slot rings; each tile is loaded two phases
-//    before it is read. LDS rows are XOR-swizzled in 16-byte chunks so that
+//    round trip) into two 3-slot rings; a K tile is issued two phases and
+//    a V tile three phases before it is first read. LDS rows are XOR-swizzled in 16-byte chunks so that
 //    the rows read by one MFMA operand fall in distinct banks.
 //  * The two waves of a SIMD run in counter-phase: while one multiplies
 //    (P.V of tile j and the scores of tile j+1: MFMAs and LDS reads only),
@@ -160,9 +160,8 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   constexpr int PV_N = DB * NB * 2; // P.V MFMAs per tile
   static_assert(PV_N == 2 * KS && NB == 2, "one score k-step (two MFMAs) per two P.V MFMAs");
 
-  // K ring (kKStages tiles), then V ring (kVStages tiles). At step j the
-  // K tile j+3 and the V tile j+1 are loaded, so every tile has two steps
-  // to land: step j reads K of tile j+1 and V of tile j-1.
+  // K ring (kKStages tiles), then V ring (kVStages tiles); the load
+  // schedule is laid out with the barriers of the main loop.
   __shared__ __attribute__((aligned(16))) char lds[(kKStages + kVStages) * G::BYTES];
   // paged K/V: the sequence's page-table row
   __shared__ int32_t pt_lds[PAGED ? kFwdPagedMaxPages : 1];
@@ -354,8 +353,8 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   // computes its softmax.
   //   slot 2j:   group 0 softmax(j),  group 1 matrix(j-1) (scores of tile 0 for j = 0)
   //   slot 2j+1: group 0 matrix(j),   group 1 softmax(j)
-  // Loads: the barrier opening slot 2j issues K tile j+2; the one opening
-  // slot 2j+1 waits for K tile j+1 and V tile j and issues V tile j+1, so
+  // Loads: the barrier opening slot 2j issues V tile j+1; the one opening
+  // slot 2j+1 waits for K tile j+1 and V tile j and issues K tile j+2, so
   // each slot carries half of the load issue.
   const int grp = wave >> 2;
   f32x16 sc[NB];   // scores of the tile being worked on
@@ -485,25 +484,25 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   __syncthreads();
   if (grp == 0) scores0();
 
-  // Barrier k opens slot k. In issue order the loads are K tile m+1 (at
-  // barrier 2m-2, the prologue for m = 0), V tile m (barrier 2m-1, the
-  // prologue for m = 0), K tile m+2 (barrier 2m).
+  // Barrier k opens slot k. In issue order the loads are V tile m (at
+  // barrier 2m-2, the prologue for m = 0), K tile m+1 (barrier 2m-1, the
+  // prologue for m = 0), V tile m+1 (barrier 2m).
   // Barrier 2m+1 waits for K tile m+1 and V tile m, read by the matrix
-  // phases of slots 2m+1 and 2m+2; only K tile m+2 may still be in flight.
-  // It then issues V tile m+1 into the slot of V tile m-2, last read in
+  // phases of slots 2m+1 and 2m+2; only V tile m+1 may still be in flight.
+  // It then issues K tile m+2 into the slot of K tile m-1, last read in
   // slot 2m-2. Barrier 2m waits for nothing (slot 2m reads tiles that
-  // barrier 2m-1 awaited) and issues K tile m+2 into the slot of K tile
-  // m-1, last read in slot 2m-2.
+  // barrier 2m-1 awaited) and issues V tile m+1 into the slot of V tile
+  // m-2, last read in slot 2m-2.
   auto barrier = [&](int k) {
     const int m = k >> 1;
     if ((k & 1) == 0) {
       __syncthreads();
-      if (m + 2 < n_kv) issue_k(m + 2);
+      if (m + 1 < n_kv) issue_v(m + 1);
     } else {
-      if (m + 2 < n_kv) __builtin_amdgcn_s_waitcnt(wait_vmcnt(LD));
+      if (m + 1 < n_kv) __builtin_amdgcn_s_waitcnt(wait_vmcnt(LD));
       else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
-      if (m + 1 < n_kv) issue_v(m + 1);
+      if (m + 2 < n_kv) issue_k(m + 2);
     }
   };
   // Each group runs its own loop; both pass barriers 0 .. 2 n_kv in order.
