@@ -70,11 +70,29 @@ struct Work {
 // Workgroup -> (sequence, query head, query tile). Consecutive workgroups
 // land on different XCDs, so the linear id is first regrouped so that XCD x
 // owns the contiguous logical range [x*per, (x+1)*per) of the work list.
-__device__ __forceinline__ Work map_block(int n_qtiles, int Hq) {
+// When that range is made of whole (sequence, head) units:
+//  * the groups of query heads that share a K/V head are dealt round-robin
+//    over the XCDs (a group stays on one XCD and in its L2; every XCD gets
+//    a share of every sequence of a ragged batch);
+//  * each XCD takes its units tile-major: the last query tile of each
+//    head first (the longest under a causal mask), then the one before,
+//    and so on, which is longest-first list scheduling over its CUs.
+__device__ __forceinline__ Work map_block(int n_qtiles, int Hq, int group) {
   const int L = blockIdx.x;
   const int total = gridDim.x;
   const int xcd = L & 7, idx = L >> 3;
   const int per = total >> 3, rem = total & 7;
+  if (rem == 0 && per % n_qtiles == 0) {
+    const int hpx = per / n_qtiles;  // (sequence, head) units per XCD
+    const int j = idx % hpx;         // unit slot of this XCD
+    const int hb = (hpx % group == 0) ? ((j / group) * 8 + xcd) * group + j % group
+                                      : xcd * hpx + j;
+    Work w;
+    w.tile = n_qtiles - 1 - idx / hpx;
+    w.h = hb % Hq;
+    w.b = hb / Hq;
+    return w;
+  }
   const int logical = xcd * per + min(xcd, rem) + idx;
   const int t = logical % n_qtiles;
   const int hb = logical / n_qtiles;
@@ -166,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   // paged K/V: the sequence's page-table row
   __shared__ int32_t pt_lds[PAGED ? kFwdPagedMaxPages : 1];
 
-  const Work w = map_block(p.n_qtiles, p.Hq);
+  const Work w = map_block(p.n_qtiles, p.Hq, p.group);
   int q0, Lq, k0, Lk;
   seq_bounds(p, w.b, q0, Lq, k0, Lk);
   const int row0 = w.tile * kBM;
@@ -557,7 +575,7 @@ __global__ __launch_bounds__(kThreads32) void fwd_f32_kernel(FwdParams p) {
   __shared__ float4 k_lds[kBN32 * D / 4];
   __shared__ float4 v_lds[kBN32 * D / 4];
 
-  const Work w = map_block(p.n_qtiles, p.Hq);
+  const Work w = map_block(p.n_qtiles, p.Hq, p.group);
   int q0, Lq, k0, Lk;
   seq_bounds(p, w.b, q0, Lq, k0, Lk);
   const int row0 = w.tile * kBM32;
