@@ -50,11 +50,14 @@ namespace fa {
 namespace {
 
 constexpr int kBM = 256;      // query rows per workgroup, 16-bit path (8 waves x 32)
-constexpr int kBN = 64;       // keys per K/V tile, 16-bit path
+#ifndef FA_KBN
+#define FA_KBN 128
+#endif
+constexpr int kBN = FA_KBN;   // keys per K/V tile, 16-bit path (64 or 128)
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kKStages = 3;   // LDS ring of K tiles
-constexpr int kVStages = 3;   // LDS ring of V tiles
+constexpr int kKStages = kBN == 64 ? 3 : 2;  // LDS ring of K tiles
+constexpr int kVStages = kBN == 64 ? 3 : 2;  // LDS ring of V tiles
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maximum.
 constexpr int kWaitVmcnt0 = 0x0F70;
 // s_waitcnt immediate: vmcnt(n) (n < 64; bits 3:0 and 15:14), expcnt and
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   constexpr int NB = kBN / 32;      // 32-key blocks per tile
   constexpr int LD = G::LOADS;      // 16-byte loads per lane per K (or V) tile
   constexpr int PV_N = DB * NB * 2; // P.V MFMAs per tile
-  static_assert(PV_N == 2 * KS && NB == 2, "one score k-step (two MFMAs) per two P.V MFMAs");
+  static_assert(PV_N == KS * NB && PV_N % 2 == 0, "as many P.V as score MFMAs per tile");
 
   // K ring (kKStages tiles), then V ring (kVStages tiles); the load
   // schedule is laid out with the barriers of the main loop.
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   // whose rows all lie inside the sequence (every tile but a ragged last
   // one): the tile base is then wave-uniform and the per-lane address
   // needs no 64-bit arithmetic. Needs kv_row * kBN * 2 bytes < 2^31.
-  const bool uniform_rows = !PAGED && p.kv_row < (1 << 24);
+  const bool uniform_rows = !PAGED && p.kv_row < (1 << 30) / kBN;
   uint32_t k_voff[LD], v_voff[LD];
 #pragma unroll
   for (int n = 0; n < LD; ++n) {
@@ -391,23 +394,26 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
-    uint4 vf[2][2], kf[2][NB];
+    // group g: P.V MFMAs m = 2g, 2g+1 and score MFMAs s = 2g, 2g+1 (k-step
+    // s / NB of 32-key block s % NB)
+    uint4 vf[2][2], kf[2][2];
     auto load_group = [&](int g, int buf) {
-      vf[buf][0] = v_frag(vst, 2 * g);
-      vf[buf][1] = v_frag(vst, 2 * g + 1);
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) kf[buf][kb] = k_frag(kst, g, kb);
+      for (int h = 0; h < 2; ++h) {
+        vf[buf][h] = v_frag(vst, 2 * g + h);
+        kf[buf][h] = k_frag(kst, (2 * g + h) / NB, (2 * g + h) % NB);
+      }
     };
     __builtin_amdgcn_s_setprio(1);
     load_group(0, 0);
 #pragma unroll
-    for (int g = 0; g < KS; ++g) {
-      if (g + 1 < KS) load_group(g + 1, (g + 1) & 1);
+    for (int g = 0; g < PV_N / 2; ++g) {
+      if (g + 1 < PV_N / 2) load_group(g + 1, (g + 1) & 1);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int m = 2 * g + h, pidx = m / DB;
         acc_o[m % DB] = E::mma32(vf[g & 1][h], pf[pidx / 2][pidx % 2], acc_o[m % DB]);
-        sc[h] = E::mma32(kf[g & 1][h], qf[g], sc[h]);
+        sc[m % NB] = E::mma32(kf[g & 1][h], qf[m / NB], sc[m % NB]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -513,14 +519,29 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   // m-2, last read in slot 2m-2.
   auto barrier = [&](int k) {
     const int m = k >> 1;
-    if ((k & 1) == 0) {
-      __syncthreads();
-      if (m + 1 < n_kv) issue_v(m + 1);
+    if constexpr (kKStages == 3) {
+      if ((k & 1) == 0) {
+        __syncthreads();
+        if (m + 1 < n_kv) issue_v(m + 1);
+      } else {
+        if (m + 1 < n_kv) __builtin_amdgcn_s_waitcnt(wait_vmcnt(LD));
+        else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (m + 2 < n_kv) issue_k(m + 2);
+      }
     } else {
-      if (m + 1 < n_kv) __builtin_amdgcn_s_waitcnt(wait_vmcnt(LD));
-      else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-      if (m + 2 < n_kv) issue_k(m + 2);
+      // two-slot rings: barrier 2m+1 waits for everything in flight (K tile
+      // m+1 and V tile m, issued at barrier 2m-1) and issues K tile m+2 and
+      // V tile m+1 into the slots of K tile m and V tile m-1, both last
+      // read in slot 2m
+      if ((k & 1) == 0) {
+        __syncthreads();
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (m + 2 < n_kv) issue_k(m + 2);
+        if (m + 1 < n_kv) issue_v(m + 1);
+      }
     }
   };
   // Each group runs its own loop; both pass barriers 0 .. 2 n_kv in order.
