@@ -189,7 +189,8 @@ size_t fa_decode_cascade_workspace_size(int B, int Hq, int d, int prefix_len, in
  *              token 0 is key prefix_len); seq_lens[b] may be 0
  *   workspace  at least fa_decode_cascade_workspace_size(...) bytes of
  *              device memory owned by the caller (scratch).
- * page_size must be 16, dtype FA_F16 or FA_BF16. Splits of 32 pages.
+ * page_size must be 16, dtype FA_F16 or FA_BF16. Prefix splits of 32 pages,
+ * suffix splits of 8 pages.
  */
 fa_status fa_decode_cascade(const void* q, const void* k_pool, const void* v_pool, void* o,
                             float* lse, const int32_t* prefix_pages, int prefix_len,

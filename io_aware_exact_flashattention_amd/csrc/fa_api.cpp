@@ -190,11 +190,13 @@ fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
 }
 
 // Splits of a cascade decode: prefix splits (32 pages each) lead, then the
-// suffix splits of the longest suffix.
+// suffix splits of the longest suffix (8 pages each: suffixes are short, so
+// shorter splits give the suffix pass enough independent work items).
+constexpr int kCascadeSuffixPagesPerSplit = 8;
 static void cascade_splits(int prefix_len, int max_pages, int& s_pre, int& s_suf) {
   const int pre_pages = (prefix_len + kPageSize - 1) / kPageSize;
   s_pre = (pre_pages + kAutoPagesPerSplit - 1) / kAutoPagesPerSplit;
-  s_suf = (max_pages + kAutoPagesPerSplit - 1) / kAutoPagesPerSplit;
+  s_suf = (max_pages + kCascadeSuffixPagesPerSplit - 1) / kCascadeSuffixPagesPerSplit;
 }
 
 size_t fa_decode_cascade_workspace_size(int B, int Hq, int d, int prefix_len, int max_pages,
@@ -230,7 +232,8 @@ fa_status fa_decode_cascade(const void* q, const void* k_pool, const void* v_poo
   p.q = q; p.k_pool = k_pool; p.v_pool = v_pool; p.o = o; p.lse = lse;
   p.page_table = page_table; p.seq_lens = seq_lens;
   p.B = B; p.max_pages = max_pages; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
-  p.pages_per_split = kAutoPagesPerSplit;
+  p.pages_per_split = kCascadeSuffixPagesPerSplit;
+  p.prefix_pages_per_split = kAutoPagesPerSplit;
   p.max_splits = s_pre + s_suf;
   p.scale_log2 = scale * kLog2e;
   p.prefix_pages = prefix_pages;

@@ -62,6 +62,34 @@ template <> struct Mma16<F16> {
   }
 };
 
+// O^T(16 d x 16 queries) += V^T(16 d x 16 tokens) * P^T(16 tokens x 16
+// queries); 4 16-bit values per lane per operand.
+template <typename T> struct Mma16k16;
+template <> struct Mma16k16<Bf16> {
+  __device__ static __forceinline__ f32x4 mma(uint2 a, uint2 b, f32x4 c) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mma16k16<F16> {
+  __device__ static __forceinline__ f32x4 mma(uint2 a, uint2 b, f32x4 c) {
+    typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h16x4, a),
+                                                 __builtin_bit_cast(h16x4, b), c, 0, 0, 0);
+  }
+};
+
+typedef short dec_s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) dec_s16x4 dec_lds_s16x4;
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane j receives
+// element j%4 of the 8 bytes addressed by lane 4e + j/4, as its element e.
+__device__ __forceinline__ uint2 lds_read_tr8(const char* lds_byte_ptr) {
+  const dec_s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (dec_lds_s16x4*)(const __attribute__((address_space(3))) char*)lds_byte_ptr);
+  return __builtin_bit_cast(uint2, v);
+}
+
 __device__ __forceinline__ float lane_value(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
@@ -103,6 +131,12 @@ __device__ __forceinline__ void settle(int& x) { asm volatile("" : "+v"(x)); }
 // P.V on the vector ALUs: lane c owns d values c*VPL .. c*VPL+VPL-1 (VPL =
 // d/64) of every head of the block for all 16 tokens, so each probability
 // is a wave-wide scalar (readlane) and no lane exchange is needed at the end.
+// The shared-prefix pass (16 query columns) does P.V on the matrix cores
+// instead: the probabilities of lane l (tokens 4(l/16)+i of query l%16) are
+// exactly its B operand of O^T += V^T P^T (v_mfma_f32_16x16x16), and V^T
+// comes from the row-major V slot with ds_read_b64_tr_b16. O^T then sits
+// in MFMA layout (lane l: query l%16, d = 16 db + 4(l/16) + i), so the
+// running max and the rescale are per lane.
 // Five waves per SIMD (five workgroups per CU) is what the LDS rings allow;
 // the widest head block needs more registers and runs four.
 template <int D, int GB> constexpr int decode_waves_per_simd() { return D * GB > 512 ? 4 : 5; }
@@ -170,9 +204,10 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
   };
   auto column_valid = [&](int c) { return !PREFIX || qb * GB + c < p.B * p.group; };
   const int npages = (L + kPage - 1) / kPage;
-  const int pg0 = s * p.pages_per_split;
+  const int pps = PREFIX ? p.prefix_pages_per_split : p.pages_per_split;
+  const int pg0 = s * pps;
   if (pg0 >= npages) return;
-  const int pg1 = min(npages, pg0 + p.pages_per_split);
+  const int pg1 = min(npages, pg0 + pps);
 
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, j = lane >> 4;  // score layout
@@ -223,15 +258,28 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
   for (int st = 0; st < KSTEP; ++st)
     kread[st] = l16 * 2 * D + 16 * ((j * (DL / 8) + st) ^ kswz<VCH>(l16));
 
-  float m[GB];          // running max per head, log2 domain (wave-uniform)
-  float o[GB][VPL];     // this lane's d values of O for each head
+  constexpr bool MFMA_PV = PREFIX;  // P.V on the matrix cores (16 columns)
+  static_assert(!MFMA_PV || GB == 16, "MFMA P.V takes 16 query columns");
+  constexpr int DB16 = D / 16;      // 16-row blocks of O^T
+  float m[MFMA_PV ? 1 : GB];        // running max per head, log2 domain (wave-uniform)
+  float o[MFMA_PV ? 1 : GB][VPL];   // this lane's d values of O for each head
+  f32x4 oacc[MFMA_PV ? DB16 : 1];   // O^T blocks in MFMA layout (MFMA_PV)
+  float m_lane = neg_inf();         // running max of query l16 (MFMA_PV)
+  if constexpr (MFMA_PV) {
 #pragma unroll
-  for (int h = 0; h < GB; ++h) {
-    m[h] = neg_inf();
+    for (int db = 0; db < DB16; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) o[h][e] = 0.f;
+    for (int h = 0; h < GB; ++h) {
+      m[h] = neg_inf();
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) o[h][e] = 0.f;
+    }
   }
   float l_lane = 0.f;   // share of the row sum of head l16 (tokens of this lane)
+  // V^T operand address of d-block db: lane a of 16-lane group g reads the
+  // 8 bytes of row 4g + a/4 at column 16 db + 4 (a % 4)
+  const int vt_off = KBYTES + (4 * j + l16 / 4) * 2 * D + 8 * (l16 & 3);
 
   issue_page(pg0, 0);
   if (NSLOT == 2 && pg0 + 1 < pg1) issue_page(pg0 + 1, 1);
@@ -244,11 +292,17 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
     uint4 kf[KSTEP];
 #pragma unroll
     for (int st = 0; st < KSTEP; ++st) kf[st] = *(const uint4*)(sp + kread[st]);
-    uint32_t vr[kPage];
+    uint32_t vr[MFMA_PV ? 1 : kPage];
+    uint2 vt[MFMA_PV ? DB16 : 1];
+    if constexpr (MFMA_PV) {
 #pragma unroll
-    for (int t = 0; t < kPage; ++t) {
-      if constexpr (VPL == 2) vr[t] = *(const uint32_t*)(sp + KBYTES + t * 2 * D + 4 * lane);
-      else vr[t] = *(const uint16_t*)(sp + KBYTES + t * 2 * D + 2 * lane);
+      for (int db = 0; db < DB16; ++db) vt[db] = lds_read_tr8(sp + vt_off + 32 * db);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kPage; ++t) {
+        if constexpr (VPL == 2) vr[t] = *(const uint32_t*)(sp + KBYTES + t * 2 * D + 4 * lane);
+        else vr[t] = *(const uint16_t*)(sp + KBYTES + t * 2 * D + 2 * lane);
+      }
     }
     wait_lds_reads();
     if (pg + NSLOT < pg1) issue_page(pg + NSLOT, slot);
@@ -256,9 +310,20 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
     const int tok0 = pg * kPage;
     // slots past the sequence end may hold anything (NaN): zero their V
     if (tok0 + kPage > L) {
+      if constexpr (MFMA_PV) {
+        // element e of vt[db] is token 4j + e
 #pragma unroll
-      for (int t = 0; t < kPage; ++t)
-        if (tok0 + t >= L) vr[t] = 0u;
+        for (int db = 0; db < DB16; ++db) {
+          if (tok0 + 4 * j + 0 >= L) vt[db].x &= 0xffff0000u;
+          if (tok0 + 4 * j + 1 >= L) vt[db].x &= 0x0000ffffu;
+          if (tok0 + 4 * j + 2 >= L) vt[db].y &= 0xffff0000u;
+          if (tok0 + 4 * j + 3 >= L) vt[db].y &= 0x0000ffffu;
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < kPage; ++t)
+          if (tok0 + t >= L) vr[t] = 0u;
+      }
     }
 
     // ---- scores S[token][head] on the matrix cores ----
@@ -275,6 +340,31 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
     }
     mx = fmaxf(mx, xor_lane(mx, 16));
     mx = fmaxf(mx, xor_lane(mx, 32));
+
+    if constexpr (MFMA_PV) {
+      // ---- running max of query l16 (same in its four token lanes) ----
+      const bool raise = mx > m_lane + kRescaleThreshold;
+      const float alpha = fast_exp2(raise ? m_lane - mx : 0.f);  // exp2(0) = 1
+      m_lane = raise ? mx : m_lane;
+      if (__ballot(raise)) {
+#pragma unroll
+        for (int db = 0; db < DB16; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[db][i] *= alpha;
+      }
+      l_lane *= alpha;
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = (sc[i] == neg_inf()) ? 0.f : fast_exp2(sc[i] - m_lane);
+        l_lane += pr[i];
+      }
+      // ---- O^T += V^T P^T on the matrix cores ----
+      const uint2 pb = make_uint2(E::pack2(pr[0], pr[1]), E::pack2(pr[2], pr[3]));
+#pragma unroll
+      for (int db = 0; db < DB16; ++db) oacc[db] = Mma16k16<T>::mma(vt[db], pb, oacc[db]);
+      continue;
+    }
 
     // ---- running max per head; rescale only when it grows by > 2^8 ----
     float m_sel = m[0], a_sel = 1.f;
@@ -316,6 +406,20 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
 
   l_lane += xor_lane(l_lane, 16);
   l_lane += xor_lane(l_lane, 32);
+  if constexpr (MFMA_PV) {
+    // lane l: query l16, d = 16 db + 4 j + i
+    if (!column_valid(l16)) return;
+    const int64_t row = q_row_of(l16) * p.max_splits + s;
+    const float inv = l_lane > 0.f ? 1.f / l_lane : 0.f;
+    float* dst = p.o_part + row * D + 4 * j;
+#pragma unroll
+    for (int db = 0; db < DB16; ++db)
+      *(float4*)(dst + 16 * db) = make_float4(oacc[db][0] * inv, oacc[db][1] * inv,
+                                              oacc[db][2] * inv, oacc[db][3] * inv);
+    if (j == 0)
+      p.lse_part[row] = l_lane > 0.f ? (m_lane + __builtin_log2f(l_lane)) * kLn2 : neg_inf();
+    return;
+  }
 #pragma unroll
   for (int h = 0; h < GB; ++h) {
     const float lt = lane_value(l_lane, h);

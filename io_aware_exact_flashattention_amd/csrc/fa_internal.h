@@ -59,6 +59,7 @@ struct DecodeParams {
   const int32_t* prefix_pages;
   int prefix_len;
   int prefix_splits;
+  int prefix_pages_per_split;  // pages per prefix split (pages_per_split: suffix splits)
   int split_offset;
 };
 

@@ -175,8 +175,9 @@ def test_cascade_rejects(lib, kw, expect):
 
 def test_cascade_workspace_size(lib):
     f = lib.fa_decode_cascade_workspace_size
-    # prefix 100 tokens = 7 pages -> 1 split; suffix 4 pages -> 1 split
+    # prefix 100 tokens = 7 pages -> 1 split of <= 32 pages; suffix 4 pages
+    # -> 1 split of <= 8 pages
     assert f(2, 4, 128, 100, 4, 16) == 2 * 4 * 2 * 129 * 4
     assert f(2, 4, 128, 0, 4, 16) == 2 * 4 * 1 * 129 * 4
-    assert f(1, 1, 64, 16384, 70, 16) == 1 * 1 * (32 + 3) * 65 * 4
+    assert f(1, 1, 64, 16384, 70, 16) == 1 * 1 * (32 + 9) * 65 * 4
     assert f(0, 4, 128, 1, 4, 16) == 0

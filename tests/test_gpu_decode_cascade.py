@@ -52,11 +52,18 @@ def test_cascade_small(dtype, d, G, prefix):
 
 
 def test_cascade_without_prefix_equals_paged_decode_bitwise():
+    """With an empty prefix the cascade is the paged decode with the same
+    split layout: its suffix splits are 8 pages, so the paged decode is asked
+    for splits of 8 pages too."""
     x = fi.cascade(0, [40, 3000, 1, 0, 700], 16, 4, 128, "bf16", seed=81)
     o1, l1 = run(x)
     p = x.pool
+    max_pages = x.page_table.shape[1]
+    ns = -(-max_pages // 8)
+    assert -(-max_pages // ns) == 8
     o2, l2 = fa.decode_paged(to_dev(x.q, "bf16"), to_dev(p.k_pool, "bf16"), to_dev(p.v_pool, "bf16"),
-                             to_dev(x.page_table, "i32"), to_dev(x.seq_lens, "i32"), scale=p.scale)
+                             to_dev(x.page_table, "i32"), to_dev(x.seq_lens, "i32"), num_splits=ns,
+                             scale=p.scale)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
