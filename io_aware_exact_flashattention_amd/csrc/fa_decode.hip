@@ -24,7 +24,8 @@
 //    denominator, so the result is unchanged.
 //  * P.V on the vector ALUs: each lane owns a 16-byte slice of the head
 //    dimension for a few tokens of the page, so V is read in its natural
-//    row layout with coalesced 16-byte loads.
+//    row layout with coalesced 16-byte loads. The shared-prefix pass of a
+//    cascade decode (16 query columns) does P.V on the matrix cores.
 //  * A second kernel merges the splits of each (sequence, query head):
 //    lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s, in fixed
 //    split order (deterministic).

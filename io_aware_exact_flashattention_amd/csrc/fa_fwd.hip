@@ -10,21 +10,25 @@
 //
 // gfx950 mapping of the 16-bit path (fwd_mfma_kernel):
 //  * A workgroup owns a 256-row Q tile: 8 wavefronts x 32 query rows, two
-//    per SIMD; K/V tiles of 64 keys.
+//    per SIMD; K/V tiles of 128 keys (64 as a compile-time option).
 //  * Scores are formed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_{bf16,f16}: the Q fragment is the B operand held in
 //    VGPRs for the whole loop, K rows come from LDS as the A operand. In the
 //    32x32 result a lane owns one query (lane % 32) and 16 of the 32 keys, so
 //    a row max / row sum is a per-lane reduction plus one exchange with
-//    lane ^ 32 - no LDS traffic for the softmax, no atomics.
+//    lane ^ 32 (v_permlane32_swap) - no LDS traffic for the softmax, no
+//    atomics.
 //  * The same lane layout is exactly the B operand of O^T += V^T P^T, so the
 //    probabilities go from the score registers to the second MFMA after a
 //    round-to-nearest conversion to 16 bits, without leaving the lane. The
 //    V^T operand is read from the row-major V tile with ds_read_b64_tr_b16.
 //  * K and V tiles reach LDS by direct-to-LDS global loads (no register
-//    round trip) into two 3-slot rings; a K tile is issued two phases and
-//    a V tile three phases before it is first read. LDS rows are XOR-swizzled in 16-byte chunks so that
-//    the rows read by one MFMA operand fall in distinct banks.
+//    round trip) into two rings (2 slots each with 128-key tiles, 3 with
+//    64-key tiles), issued at least two phases before they are first read.
+//    A tile whose rows all lie inside the sequence is addressed from a
+//    wave-uniform base plus a 32-bit lane offset. LDS rows are XOR-swizzled
+//    in 16-byte chunks so that the rows read by one MFMA operand fall in
+//    distinct banks.
 //  * The two waves of a SIMD run in counter-phase: while one multiplies
 //    (P.V of tile j and the scores of tile j+1: MFMAs and LDS reads only),
 //    the other computes the softmax of its tile (vector ALUs only), and a
@@ -34,10 +38,10 @@
 //    more than 2^8 (weights stay below 2^8 in fp32), so most tiles skip the
 //    rescale of the output accumulator; numerator and denominator share the
 //    reference, so the result equals the exact running-max recurrence.
-//  * Workgroup ids are remapped so that each XCD (workgroups are dealt out
-//    round-robin over the 8 XCDs) gets a contiguous run of (sequence, head)
-//    units, keeping a head's K/V in that XCD's L2; inside a head the query
-//    tiles run longest (last, under a causal mask) first.
+//  * Workgroup ids are remapped (workgroups are dealt out round-robin over
+//    the 8 XCDs): the groups of query heads that share a K/V head go
+//    round-robin over the XCDs, keeping that K/V in one XCD's L2, and each
+//    XCD runs its query tiles longest (last, under a causal mask) first.
 //  * Causal: K/V tiles that no row of the Q tile may see are never loaded;
 //    only tiles that cross the diagonal or the sequence end are masked.
 //
