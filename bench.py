@@ -223,7 +223,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
-              f"(this build runs on a single MI355X)", file=sys.stderr)
+              f"(it runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
