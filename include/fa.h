@@ -140,7 +140,7 @@ size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_pages, int p
  *              or beyond ceil(seq_lens[b]/page_size) are not read
  *   seq_lens   device int32 [B], 0 <= seq_lens[b] <= max_pages*page_size
  *   o [B, Hq, d] dtype, lse [B, Hq] float32 (written)
- *   num_splits 0 = automatic (32 pages per split), else the number of key
+ *   num_splits 0 = automatic (48 pages per split), else the number of key
  *              splits of the longest sequence (1 .. max_pages); a split never
  *              holds more than 64 pages, so smaller values are raised to
  *              ceil(max_pages / 64)

@@ -12,7 +12,14 @@
 namespace {
 
 constexpr int kPageSize = 16;
-constexpr int kAutoPagesPerSplit = 32;
+// Pages per split of a plain decode without a split count. 43-50 pages gave
+// the highest K/V read rate on MI355X for 64 sequences of U[512, 32768]
+// tokens (about 3% above 32 pages): fewer partial results and item
+// start-ups, while the ~2.8 rounds of work items still let the dispatcher
+// balance the ragged lengths.
+constexpr int kDecodePagesPerSplit = 48;
+// Pages per split of the shared-prefix pass of a cascade decode.
+constexpr int kPrefixPagesPerSplit = 32;
 constexpr int kMaxPagesPerSplit = 64;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -136,11 +143,12 @@ fa_status fa_fwd_paged(const void* q, const void* k_pool, const void* v_pool, vo
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-// Pages per split: 32 when automatic; otherwise the longest sequence is cut
-// into num_splits ranges, but a range never exceeds kMaxPagesPerSplit pages
-// (the decode kernel holds one split's page indices in the lanes of a wave).
+// Pages per split: kDecodePagesPerSplit when automatic; otherwise the
+// longest sequence is cut into num_splits ranges, but a range never exceeds
+// kMaxPagesPerSplit pages (the decode kernel holds one split's page indices
+// in the lanes of a wave).
 static int pages_per_split(int max_pages, int num_splits) {
-  if (num_splits <= 0) return kAutoPagesPerSplit;
+  if (num_splits <= 0) return kDecodePagesPerSplit;
   const int pps = (max_pages + num_splits - 1) / num_splits;
   return pps < kMaxPagesPerSplit ? pps : kMaxPagesPerSplit;
 }
@@ -195,7 +203,7 @@ fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
 constexpr int kCascadeSuffixPagesPerSplit = 8;
 static void cascade_splits(int prefix_len, int max_pages, int& s_pre, int& s_suf) {
   const int pre_pages = (prefix_len + kPageSize - 1) / kPageSize;
-  s_pre = (pre_pages + kAutoPagesPerSplit - 1) / kAutoPagesPerSplit;
+  s_pre = (pre_pages + kPrefixPagesPerSplit - 1) / kPrefixPagesPerSplit;
   s_suf = (max_pages + kCascadeSuffixPagesPerSplit - 1) / kCascadeSuffixPagesPerSplit;
 }
 
@@ -233,7 +241,7 @@ fa_status fa_decode_cascade(const void* q, const void* k_pool, const void* v_poo
   p.page_table = page_table; p.seq_lens = seq_lens;
   p.B = B; p.max_pages = max_pages; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
   p.pages_per_split = kCascadeSuffixPagesPerSplit;
-  p.prefix_pages_per_split = kAutoPagesPerSplit;
+  p.prefix_pages_per_split = kPrefixPagesPerSplit;
   p.max_splits = s_pre + s_suf;
   p.scale_log2 = scale * kLog2e;
   p.prefix_pages = prefix_pages;

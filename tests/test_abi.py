@@ -104,8 +104,8 @@ def test_decode_rejects(lib, kw, expect):
 
 def test_workspace_size(lib):
     f = lib.fa_decode_paged_workspace_size
-    # auto split: 32 pages per split
-    assert f(64, 32, 128, 2017, 16, 0) == 64 * 32 * 64 * 129 * 4
+    # auto split: 48 pages per split
+    assert f(64, 32, 128, 2017, 16, 0) == 64 * 32 * 43 * 129 * 4
     assert f(2, 4, 64, 10, 16, 3) == 2 * 4 * 3 * 65 * 4        # ceil(10/3)=4 pages -> 3 splits
     assert f(2, 4, 64, 10, 16, 1) == 2 * 4 * 1 * 65 * 4
     # a split holds at most 64 pages: one split over 200 pages becomes 4

@@ -64,6 +64,20 @@ def test_decode_split_counts(num_splits):
     check(x, f"decode splits={num_splits}", num_splits=num_splits)
 
 
+def test_decode_many_sequences_balanced():
+    """More sequences than one wavefront's lanes (two steps of the 64-way
+    search for the first sequence of a wavefront's range), empty ones among
+    them, and wavefront ranges that cross sequence and head boundaries."""
+    rng = np.random.default_rng(46)
+    lens = rng.integers(0, 700, 300)
+    lens[rng.random(300) < 0.15] = 0
+    x = fi.paged(lens, 8, 2, 128, "bf16", seed=46)
+    o, l = run(x)
+    empty = np.flatnonzero(lens == 0)
+    assert np.all(to_f64(o)[empty] == 0) and np.all(to_f64(l)[empty] == -np.inf)
+    check(x, "decode 300 sequences", seqs=np.flatnonzero(lens > 0))
+
+
 def test_decode_zero_length_sequence():
     lens = [0, 20, 0, 300]
     x = fi.paged(lens, 8, 2, 128, "bf16", seed=42)
