@@ -45,8 +45,9 @@
 //  * Causal: K/V tiles that no row of the Q tile may see are never loaded;
 //    only tiles that cross the diagonal or the sequence end are masked.
 //
-// fp32 inputs take fwd_f32_kernel: the same tiling and online softmax on
-// the vector ALUs (4 lanes per query row), for exact fp32 arithmetic.
+// fp32 inputs take fwd_f32_kernel: the same online softmax on the vector
+// ALUs (4 lanes per query row), for exact fp32 arithmetic, with the key
+// range of a 32-row tile shared by four groups of threads and merged.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -590,15 +591,24 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
 }
 
 // ------------------------------------------------------------------ fp32 --
-constexpr int kBM32 = 32;  // query rows per workgroup
-constexpr int kBN32 = 32;  // keys per tile
-constexpr int kThreads32 = 128;
+constexpr int kBM32 = 32;     // query rows per workgroup
+constexpr int kBN32 = 32;     // keys per tile
+constexpr int kSplit32 = 4;   // key splits of a workgroup
+constexpr int kThreads32 = 128 * kSplit32;
 
+// Exact fp32 path on the vector ALUs. A workgroup owns 32 query rows; each
+// of its kSplit32 groups of 128 threads (4 lanes per row, D/4 values of d
+// per lane) runs the online softmax over every kSplit32-th K/V tile of the
+// rows' key range, starting at its own index (so a causal range is shared
+// evenly). The groups' states (m, l, O) are then merged in a fixed order,
+// the same log-sum-exp algebra as the split merge of the decode.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads32) void fwd_f32_kernel(FwdParams p) {
-  constexpr int DQ = D / 4;  // d values per lane (4 lanes per query row)
-  __shared__ float4 k_lds[kBN32 * D / 4];
-  __shared__ float4 v_lds[kBN32 * D / 4];
+  constexpr int DQ = D / 4;              // d values per lane (4 lanes per query row)
+  constexpr int TILE4 = kBN32 * D / 4;   // float4 per K (or V) tile
+  constexpr int RED = DQ + 2;            // floats per thread in the merge: m, l, O
+  static_assert(kThreads32 * RED <= kSplit32 * 2 * TILE4 * 4, "merge fits in the tile buffers");
+  __shared__ float4 kv_lds[kSplit32][2][TILE4];  // per split: K tile, V tile
 
   const Work w = map_block(p.n_qtiles, p.Hq, p.group);
   int q0, Lq, k0, Lk;
@@ -607,8 +617,10 @@ __global__ __launch_bounds__(kThreads32) void fwd_f32_kernel(FwdParams p) {
   if (row0 >= Lq) return;
   const int g = w.h / p.group;
   const int tid = threadIdx.x;
-  const int quad = tid & 3;
-  const int my_row = row0 + (tid >> 2);
+  const int split = __builtin_amdgcn_readfirstlane(tid >> 7);  // two whole waves per split
+  const int t = tid & 127;
+  const int quad = t & 3;
+  const int my_row = row0 + (t >> 2);
   const int delta = Lk - Lq;
 
   int kv_end = Lk;
@@ -620,8 +632,8 @@ __global__ __launch_bounds__(kThreads32) void fwd_f32_kernel(FwdParams p) {
     const float* src = (const float*)p.q + (int64_t)(q0 + my_row) * p.q_row + (int64_t)w.h * D + quad * DQ;
 #pragma unroll
     for (int i = 0; i < DQ; i += 4) {
-      const float4 t = *(const float4*)(src + i);
-      q[i] = t.x; q[i + 1] = t.y; q[i + 2] = t.z; q[i + 3] = t.w;
+      const float4 x = *(const float4*)(src + i);
+      q[i] = x.x; q[i + 1] = x.y; q[i + 2] = x.z; q[i + 3] = x.w;
     }
   } else {
 #pragma unroll
@@ -629,25 +641,33 @@ __global__ __launch_bounds__(kThreads32) void fwd_f32_kernel(FwdParams p) {
   }
 #pragma unroll
   for (int i = 0; i < DQ; ++i) o[i] = 0.f;
-  float m_run = neg_inf(), l_run = 0.f;
+  float m_run = neg_inf(), l_run = 0.f;  // log2 domain
   const float c2 = p.scale_log2;
   const float* kbase = (const float*)p.k + (int64_t)k0 * p.kv_row + (int64_t)g * D;
   const float* vbase = (const float*)p.v + (int64_t)k0 * p.kv_row + (int64_t)g * D;
+  const float4* k_lds = kv_lds[split][0];
+  const float4* v_lds = kv_lds[split][1];
 
-  for (int j = 0; j < n_kv; ++j) {
+  const int n_iter = (n_kv + kSplit32 - 1) / kSplit32;
+  for (int it = 0; it < n_iter; ++it) {
+    const int j = it * kSplit32 + split;  // this split's tile
+    const bool have = j < n_kv;           // uniform over the split
     __syncthreads();
-    for (int u = tid; u < kBN32 * D / 4; u += kThreads32) {
-      const int r = u / (D / 4), c = u % (D / 4);
-      const int key = j * kBN32 + r;
-      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-      if (key < Lk) {
-        kv = *(const float4*)(kbase + (int64_t)key * p.kv_row + 4 * c);
-        vv = *(const float4*)(vbase + (int64_t)key * p.kv_row + 4 * c);
+    if (have) {
+      for (int u = t; u < TILE4; u += 128) {
+        const int r = u / (D / 4), c = u % (D / 4);
+        const int key = j * kBN32 + r;
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+        if (key < Lk) {
+          kv = *(const float4*)(kbase + (int64_t)key * p.kv_row + 4 * c);
+          vv = *(const float4*)(vbase + (int64_t)key * p.kv_row + 4 * c);
+        }
+        kv_lds[split][0][u] = kv;
+        kv_lds[split][1][u] = vv;
       }
-      k_lds[u] = kv;
-      v_lds[u] = vv;
     }
     __syncthreads();
+    if (!have) continue;
 
     float s[kBN32];
 #pragma unroll
@@ -697,15 +717,43 @@ __global__ __launch_bounds__(kThreads32) void fwd_f32_kernel(FwdParams p) {
     }
   }
 
+  // ---- merge the splits (fixed order), then O = O / l, LSE ----
+  float* red = (float*)&kv_lds[0][0][0];
+  __syncthreads();  // every split is done with its tiles
+  {
+    float* mine = red + (int64_t)tid * RED;
+    mine[0] = m_run;
+    mine[1] = l_run;
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) mine[2 + i] = o[i];
+  }
+  __syncthreads();
+  if (split != 0) return;
+  float M = neg_inf();
+#pragma unroll
+  for (int sp = 0; sp < kSplit32; ++sp) M = fmaxf(M, red[(sp * 128 + t) * RED]);
+  float l_tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) o[i] = 0.f;
+  if (M != neg_inf()) {
+#pragma unroll
+    for (int sp = 0; sp < kSplit32; ++sp) {
+      const float* st = red + (sp * 128 + t) * RED;
+      const float ws = st[0] == neg_inf() ? 0.f : fast_exp2(st[0] - M);
+      l_tot = fmaf(st[1], ws, l_tot);
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) o[i] = fmaf(st[2 + i], ws, o[i]);
+    }
+  }
   if (my_row < Lq) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float* dst = (float*)p.o + (int64_t)(q0 + my_row) * p.q_row + (int64_t)w.h * D + quad * DQ;
 #pragma unroll
     for (int i = 0; i < DQ; i += 4)
       *(float4*)(dst + i) = make_float4(o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv);
     if (quad == 0)
       p.lse[(int64_t)(q0 + my_row) * p.Hq + w.h] =
-          l_run > 0.f ? (m_run + __builtin_log2f(l_run)) * kLn2 : neg_inf();
+          l_tot > 0.f ? (M + __builtin_log2f(l_tot)) * kLn2 : neg_inf();
   }
 }
 
