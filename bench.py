@@ -120,7 +120,7 @@ def other_configs(torch, fa, fi, to_dev, dev, reps=20):
     res = {}
 
     def timed(fn):
-        for _ in range(3):
+        for _ in range(10):  # clocks ramp up after the small cases before
             fn()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

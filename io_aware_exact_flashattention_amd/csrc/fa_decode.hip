@@ -25,7 +25,7 @@
 //  * P.V on the vector ALUs: each lane owns a 16-byte slice of the head
 //    dimension for a few tokens of the page, so V is read in its natural
 //    row layout with coalesced 16-byte loads. The shared-prefix pass of a
-//    cascade decode (16 query columns) does P.V on the matrix cores.
+//    cascade decode (32 query columns) does P.V on the matrix cores.
 //  * A second kernel merges the splits of each (sequence, query head):
 //    lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s, in fixed
 //    split order (deterministic).
@@ -132,23 +132,29 @@ __device__ __forceinline__ void settle(int& x) { asm volatile("" : "+v"(x)); }
 // P.V on the vector ALUs: lane c owns d values c*VPL .. c*VPL+VPL-1 (VPL =
 // d/64) of every head of the block for all 16 tokens, so each probability
 // is a wave-wide scalar (readlane) and no lane exchange is needed at the end.
-// The shared-prefix pass (16 query columns) does P.V on the matrix cores
+// The shared-prefix pass (blocks of 16 query columns) does P.V on the matrix cores
 // instead: the probabilities of lane l (tokens 4(l/16)+i of query l%16) are
 // exactly its B operand of O^T += V^T P^T (v_mfma_f32_16x16x16), and V^T
 // comes from the row-major V slot with ds_read_b64_tr_b16. O^T then sits
 // in MFMA layout (lane l: query l%16, d = 16 db + 4(l/16) + i), so the
 // running max and the rescale are per lane.
 // Five waves per SIMD (five workgroups per CU) is what the LDS rings allow;
-// the widest head block needs more registers and runs four.
-template <int D, int GB> constexpr int decode_waves_per_simd() { return D * GB > 512 ? 4 : 5; }
+// the widest head block needs more registers and runs four, the 32-column
+// prefix pass at d = 128 three.
+template <int D, int GB, bool PREFIX>
+constexpr int decode_waves_per_simd() {
+  return PREFIX ? (D == 128 ? 3 : 4) : (D * GB > 512 ? 4 : 5);
+}
 
 // PREFIX: the shared-prefix pass of a cascade decode. A work item is then
-// (block of 16 query columns, prefix split, KV head); column c of block qb is
-// query r = 16 qb + c of the r-th (sequence, head-in-group) pair of the KV
-// head, so the prefix pages are read once for every query of the group.
+// (block of 32 query columns, prefix split, KV head); column c of block qb is
+// query r = 32 qb + c of the r-th (sequence, head-in-group) pair of the KV
+// head, so the prefix pages are read once for every 32 queries of the group.
+// The 32 columns are two 16-column MFMA operands that share each page's K
+// and V fragments.
 template <typename T, int D, int GB, bool PREFIX = false>
 __global__ __launch_bounds__(64 * kWavesPerBlock)
-__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode_split_kernel(
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB, PREFIX>()))) void decode_split_kernel(
     DecodeParams p) {
   using E = Elem<T>;
   constexpr int KSTEP = D / 32;       // MFMA k-steps per page (K loads per page)
@@ -161,6 +167,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
   constexpr int SLOT = 2 * KBYTES;
   constexpr int NSLOT = kWaveLds / SLOT;
   constexpr int VPL = D / 64;         // d values per lane in P.V
+  constexpr int NCB = PREFIX ? 2 : 1; // 16-column blocks of an item (prefix pass: 32 queries)
   static_assert(GB <= 16 && VI >= 1 && (NSLOT == 1 || NSLOT == 2), "bad decode tile");
   static_assert(KSTEP * 1024 == KBYTES && VI * 1024 == KBYTES, "page layout");
   __shared__ uint4 lds[kWavesPerBlock][kWaveLds / 16];
@@ -175,7 +182,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
     item /= p.Hkv;
     s = item % p.prefix_splits;
     qb = item / p.prefix_splits;
-    if (qb * GB >= p.B * p.group) return;
+    if (qb * GB * NCB >= p.B * p.group) return;
     b = 0;
     h0 = 0;
     L = p.prefix_len;
@@ -198,12 +205,12 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
   // query row (sequence * Hq + head) of column c
   auto q_row_of = [&](int c) -> int64_t {
     if (PREFIX) {
-      const int r = qb * GB + c;
+      const int r = qb * GB * NCB + c;
       return (int64_t)(r / p.group) * p.Hq + g * p.group + r % p.group;
     }
     return (int64_t)b * p.Hq + h0 + c;
   };
-  auto column_valid = [&](int c) { return !PREFIX || qb * GB + c < p.B * p.group; };
+  auto column_valid = [&](int c) { return !PREFIX || qb * GB * NCB + c < p.B * p.group; };
   const int npages = (L + kPage - 1) / kPage;
   const int pps = PREFIX ? p.prefix_pages_per_split : p.pages_per_split;
   const int pg0 = s * pps;
@@ -214,20 +221,26 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
   const int l16 = lane & 15, j = lane >> 4;  // score layout
   const float c2 = p.scale_log2;
 
-  // B operand: Q^T, columns 0..GB-1 (zero for absent queries)
-  uint4 qf[KSTEP];
+  // B operands: Q^T, columns 16 cb + 0 .. 16 cb + GB-1 of column block cb
+  // (zero for absent queries)
+  uint4 qf[NCB][KSTEP];
 #pragma unroll
-  for (int st = 0; st < KSTEP; ++st) qf[st] = make_uint4(0, 0, 0, 0);
-  if (l16 < GB && column_valid(l16)) {
-    const uint16_t* src = (const uint16_t*)p.q + q_row_of(l16) * D + j * DL;
+  for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-    for (int st = 0; st < KSTEP; ++st) qf[st] = *(const uint4*)(src + 8 * st);
+    for (int st = 0; st < KSTEP; ++st) qf[cb][st] = make_uint4(0, 0, 0, 0);
+    if (l16 < GB && column_valid(16 * cb + l16)) {
+      const uint16_t* src = (const uint16_t*)p.q + q_row_of(16 * cb + l16) * D + j * DL;
+#pragma unroll
+      for (int st = 0; st < KSTEP; ++st) qf[cb][st] = *(const uint4*)(src + 8 * st);
+    }
   }
   // Page indices of the split (at most 64 pages): lane i holds entry
   // pg0 + i; each page's index is read from its lane.
   int pg_idx = pg0 + lane < pg1 ? pt[pg0 + lane] : 0;
 #pragma unroll
-  for (int st = 0; st < KSTEP; ++st) settle(qf[st]);
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int st = 0; st < KSTEP; ++st) settle(qf[cb][st]);
   settle(pg_idx);
 
   // Direct-to-LDS copies of whole token rows (each load instruction reads
@@ -259,16 +272,20 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
   for (int st = 0; st < KSTEP; ++st)
     kread[st] = l16 * 2 * D + 16 * ((j * (DL / 8) + st) ^ kswz<VCH>(l16));
 
-  constexpr bool MFMA_PV = PREFIX;  // P.V on the matrix cores (16 columns)
+  constexpr bool MFMA_PV = PREFIX;  // P.V on the matrix cores (16 columns per block)
   static_assert(!MFMA_PV || GB == 16, "MFMA P.V takes 16 query columns");
   constexpr int DB16 = D / 16;      // 16-row blocks of O^T
   float m[MFMA_PV ? 1 : GB];        // running max per head, log2 domain (wave-uniform)
   float o[MFMA_PV ? 1 : GB][VPL];   // this lane's d values of O for each head
-  f32x4 oacc[MFMA_PV ? DB16 : 1];   // O^T blocks in MFMA layout (MFMA_PV)
-  float m_lane = neg_inf();         // running max of query l16 (MFMA_PV)
+  f32x4 oacc[NCB][MFMA_PV ? DB16 : 1];  // O^T blocks in MFMA layout (MFMA_PV)
+  float m_lane[NCB];                // running max of query 16 cb + l16 (MFMA_PV)
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) m_lane[cb] = neg_inf();
   if constexpr (MFMA_PV) {
 #pragma unroll
-    for (int db = 0; db < DB16; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int db = 0; db < DB16; ++db) oacc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   } else {
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
@@ -277,7 +294,9 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
       for (int e = 0; e < VPL; ++e) o[h][e] = 0.f;
     }
   }
-  float l_lane = 0.f;   // share of the row sum of head l16 (tokens of this lane)
+  float l_lane[NCB];    // share of the row sum of column 16 cb + l16 (tokens of this lane)
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) l_lane[cb] = 0.f;
   // V^T operand address of d-block db: lane a of 16-lane group g reads the
   // 8 bytes of row 4g + a/4 at column 16 db + 4 (a % 4)
   const int vt_off = KBYTES + (4 * j + l16 / 4) * 2 * D + 8 * (l16 & 3);
@@ -327,43 +346,51 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
       }
     }
 
-    // ---- scores S[token][head] on the matrix cores ----
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- scores S[token][column] on the matrix cores, per column block ----
+    float sc[NCB][4];
+    float mx[NCB];
 #pragma unroll
-    for (int st = 0; st < KSTEP; ++st) acc = Mma16<T>::mma(kf[st], qf[st], acc);
-    float sc[4];
-    float mx = neg_inf();
+    for (int cb = 0; cb < NCB; ++cb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = (l16 < GB) && (tok0 + 4 * j + i < L);
-      sc[i] = ok ? acc[i] * c2 : neg_inf();
-      mx = fmaxf(mx, sc[i]);
-    }
-    mx = fmaxf(mx, xor_lane(mx, 16));
-    mx = fmaxf(mx, xor_lane(mx, 32));
-
-    if constexpr (MFMA_PV) {
-      // ---- running max of query l16 (same in its four token lanes) ----
-      const bool raise = mx > m_lane + kRescaleThreshold;
-      const float alpha = fast_exp2(raise ? m_lane - mx : 0.f);  // exp2(0) = 1
-      m_lane = raise ? mx : m_lane;
-      if (__ballot(raise)) {
-#pragma unroll
-        for (int db = 0; db < DB16; ++db)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[db][i] *= alpha;
-      }
-      l_lane *= alpha;
-      float pr[4];
+      for (int st = 0; st < KSTEP; ++st) acc = Mma16<T>::mma(kf[st], qf[cb][st], acc);
+      mx[cb] = neg_inf();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pr[i] = (sc[i] == neg_inf()) ? 0.f : fast_exp2(sc[i] - m_lane);
-        l_lane += pr[i];
+        const bool ok = (l16 < GB) && (tok0 + 4 * j + i < L);
+        sc[cb][i] = ok ? acc[i] * c2 : neg_inf();
+        mx[cb] = fmaxf(mx[cb], sc[cb][i]);
       }
-      // ---- O^T += V^T P^T on the matrix cores ----
-      const uint2 pb = make_uint2(E::pack2(pr[0], pr[1]), E::pack2(pr[2], pr[3]));
+      mx[cb] = fmaxf(mx[cb], xor_lane(mx[cb], 16));
+      mx[cb] = fmaxf(mx[cb], xor_lane(mx[cb], 32));
+    }
+
+    if constexpr (MFMA_PV) {
 #pragma unroll
-      for (int db = 0; db < DB16; ++db) oacc[db] = Mma16k16<T>::mma(vt[db], pb, oacc[db]);
+      for (int cb = 0; cb < NCB; ++cb) {
+        // ---- running max of query 16 cb + l16 (same in its four token lanes) ----
+        const bool raise = mx[cb] > m_lane[cb] + kRescaleThreshold;
+        const float alpha = fast_exp2(raise ? m_lane[cb] - mx[cb] : 0.f);  // exp2(0) = 1
+        m_lane[cb] = raise ? mx[cb] : m_lane[cb];
+        if (__ballot(raise)) {
+#pragma unroll
+          for (int db = 0; db < DB16; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[cb][db][i] *= alpha;
+        }
+        l_lane[cb] *= alpha;
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pr[i] = (sc[cb][i] == neg_inf()) ? 0.f : fast_exp2(sc[cb][i] - m_lane[cb]);
+          l_lane[cb] += pr[i];
+        }
+        // ---- O^T += V^T P^T on the matrix cores ----
+        const uint2 pb = make_uint2(E::pack2(pr[0], pr[1]), E::pack2(pr[2], pr[3]));
+#pragma unroll
+        for (int db = 0; db < DB16; ++db)
+          oacc[cb][db] = Mma16k16<T>::mma(vt[db], pb, oacc[cb][db]);
+      }
       continue;
     }
 
@@ -371,7 +398,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
     float m_sel = m[0], a_sel = 1.f;
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
-      const float pm = lane_value(mx, h);
+      const float pm = lane_value(mx[0], h);
       if (pm > m[h] + kRescaleThreshold) {
         const float alpha = fast_exp2(m[h] - pm);
         m[h] = pm;
@@ -381,13 +408,13 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
       }
       if (l16 == h) m_sel = m[h];
     }
-    l_lane *= a_sel;
+    l_lane[0] *= a_sel;
 
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pr[i] = (sc[i] == neg_inf()) ? 0.f : fast_exp2(sc[i] - m_sel);
-      l_lane += pr[i];
+      pr[i] = (sc[0][i] == neg_inf()) ? 0.f : fast_exp2(sc[0][i] - m_sel);
+      l_lane[0] += pr[i];
     }
 
     // ---- O += P V: P[t][h] sits in register t%4 of lane 16(t/4) + h ----
@@ -405,25 +432,33 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB>()))) void decode
     }
   }
 
-  l_lane += xor_lane(l_lane, 16);
-  l_lane += xor_lane(l_lane, 32);
-  if constexpr (MFMA_PV) {
-    // lane l: query l16, d = 16 db + 4 j + i
-    if (!column_valid(l16)) return;
-    const int64_t row = q_row_of(l16) * p.max_splits + s;
-    const float inv = l_lane > 0.f ? 1.f / l_lane : 0.f;
-    float* dst = p.o_part + row * D + 4 * j;
 #pragma unroll
-    for (int db = 0; db < DB16; ++db)
-      *(float4*)(dst + 16 * db) = make_float4(oacc[db][0] * inv, oacc[db][1] * inv,
-                                              oacc[db][2] * inv, oacc[db][3] * inv);
-    if (j == 0)
-      p.lse_part[row] = l_lane > 0.f ? (m_lane + __builtin_log2f(l_lane)) * kLn2 : neg_inf();
+  for (int cb = 0; cb < NCB; ++cb) {
+    l_lane[cb] += xor_lane(l_lane[cb], 16);
+    l_lane[cb] += xor_lane(l_lane[cb], 32);
+  }
+  if constexpr (MFMA_PV) {
+    // lane l: query 16 cb + l16, d = 16 db + 4 j + i
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      if (!column_valid(16 * cb + l16)) continue;
+      const int64_t row = q_row_of(16 * cb + l16) * p.max_splits + s;
+      const float inv = l_lane[cb] > 0.f ? 1.f / l_lane[cb] : 0.f;
+      float* dst = p.o_part + row * D + 4 * j;
+#pragma unroll
+      for (int db = 0; db < DB16; ++db)
+        *(float4*)(dst + 16 * db) =
+            make_float4(oacc[cb][db][0] * inv, oacc[cb][db][1] * inv, oacc[cb][db][2] * inv,
+                        oacc[cb][db][3] * inv);
+      if (j == 0)
+        p.lse_part[row] =
+            l_lane[cb] > 0.f ? (m_lane[cb] + __builtin_log2f(l_lane[cb])) * kLn2 : neg_inf();
+    }
     return;
   }
 #pragma unroll
   for (int h = 0; h < GB; ++h) {
-    const float lt = lane_value(l_lane, h);
+    const float lt = lane_value(l_lane[0], h);
     if (!column_valid(h)) continue;
     const int64_t row = q_row_of(h) * p.max_splits + (PREFIX ? 0 : p.split_offset) + s;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -510,8 +545,9 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
 template <typename T, int D, int GB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t st) {
   if (p.prefix_len > 0) {
-    constexpr int QB = 16;
-    const int64_t items = (int64_t)((p.B * p.group + QB - 1) / QB) * p.prefix_splits * p.Hkv;
+    constexpr int QB = 16;  // columns per MFMA block; an item takes two blocks
+    const int64_t items =
+        (int64_t)((p.B * p.group + 2 * QB - 1) / (2 * QB)) * p.prefix_splits * p.Hkv;
     const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
     hipLaunchKernelGGL((decode_split_kernel<T, D, QB, true>), dim3(blocks),
                        dim3(64 * kWavesPerBlock), 0, st, p);
