@@ -181,6 +181,24 @@ def other_configs(torch, fa, fi, to_dev, dev, reps=20):
         "dtype": "bf16", "ms_mean": mean, "ms_min": mn, "tflops": tf,
         "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
 
+    # appending the chunks' K/V rows to the paged cache (the step before the
+    # chunked prefill above): bytes = K and V rows read once and written once
+    lens_before = (lk - lq).astype(np.int32)
+    cu_new = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    k_new = np.concatenate([kv.k_seq[kv.cu_k[s] + lens_before[s]:kv.cu_k[s + 1]] for s in range(len(lq))])
+    v_new = np.concatenate([kv.v_seq[kv.cu_k[s] + lens_before[s]:kv.cu_k[s + 1]] for s in range(len(lq))])
+    kn, vn = to_dev(k_new, "bf16"), to_dev(v_new, "bf16")
+    cn, lb = to_dev(cu_new, "i32"), to_dev(lens_before, "i32")
+    a_mean, a_min = timed(lambda: fa.kv_append(kn, vn, kp, vp, cn, pt, lb))
+    moved = 2 * 2 * k_new.size * 2  # K and V, read and written, 2 bytes each
+    res["kv_append_chunks"] = {
+        "workload": "fa_kv_append: the 16 chunks above (U[1,2048] tokens after cached prefixes "
+                    "U[0,8192]) written into the permuted page pool, Hkv=8 d=128",
+        "dtype": "bf16", "ms_mean": a_mean, "ms_min": a_min, "tokens": int(k_new.shape[0]),
+        "gbs": moved / (a_mean * 1e-3) / 1e9, "peak_gbs": PEAK_HBM_GBS,
+        "frac": moved / (a_mean * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del kn, vn, cn, lb
+
     # shared-prompt decode: 64 sequences on one 16384-token prefix; the
     # unique K/V bytes (prefix once + suffixes) and the bytes a plain paged
     # decode would read (prefix once per sequence)

@@ -6,20 +6,23 @@
 // sequence that holds L writes token i to position L + i: page
 // page_table[s][(L+i) / 16], slot (L+i) % 16. The kernel moves bits only.
 //
-// One workgroup per new token (grid x) and per tensor (grid y: 0 = K, 1 = V);
-// its threads copy the token row (Hkv * d values, a multiple of 16 bytes) in
-// 16-byte pieces. This is a pure HBM copy: 2 x row bytes read and written
-// per token and tensor.
+// One wavefront per new token and tensor: workgroups of four wavefronts
+// take four consecutive tokens (grid x), grid y picks the tensor (0 = K,
+// 1 = V). A wavefront finds the token's sequence, then copies the token row
+// (Hkv * d values, a multiple of 16 bytes) in 16-byte pieces. This is a pure
+// HBM copy: 2 x row bytes read and written per token and tensor.
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-constexpr int kAppendThreads = 256;
+constexpr int kAppendWaves = 4;
 
-__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) {
-  const int t = blockIdx.x;  // token of the batch
+__global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(AppendParams p, int T_new) {
+  const int t = blockIdx.x * kAppendWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= T_new) return;
+  const int lane = threadIdx.x & 63;
   const bool is_v = blockIdx.y != 0;
   // its sequence: cu_new[s] <= t < cu_new[s+1] (cu_new non-decreasing, cu_new[0] = 0,
   // cu_new[B] = T_new > t)
@@ -40,14 +43,14 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
   const char* src = (const char*)(is_v ? p.v_new : p.k_new) + (int64_t)t * p.row_bytes;
   char* dst = (char*)(is_v ? p.v_pool : p.k_pool) + row * p.row_bytes;
   const int chunks = (int)(p.row_bytes / 16);
-  for (int c = threadIdx.x; c < chunks; c += kAppendThreads)
-    ((uint4*)dst)[c] = ((const uint4*)src)[c];
+  for (int c = lane; c < chunks; c += 64) ((uint4*)dst)[c] = ((const uint4*)src)[c];
 }
 
 }  // namespace
 
 hipError_t launch_append(const AppendParams& p, int T_new, hipStream_t st) {
-  hipLaunchKernelGGL(append_kernel, dim3(T_new, 2), dim3(kAppendThreads), 0, st, p);
+  hipLaunchKernelGGL(append_kernel, dim3((T_new + kAppendWaves - 1) / kAppendWaves, 2),
+                     dim3(64 * kAppendWaves), 0, st, p, T_new);
   return hipGetLastError();
 }
 
