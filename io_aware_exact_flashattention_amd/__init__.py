@@ -1,17 +1,26 @@
 """MI355X (gfx950) exact attention forward: Python binding of libfa_amd.so.
 
-Three entry points, each returning (O, LSE) and each one call into the C ABI
-(include/fa.h), enqueued on torch's current HIP stream:
+Each function is one call into the C ABI (include/fa.h), enqueued on torch's
+current HIP stream; the attention calls return (O, LSE):
 
 * ``fwd(q, k, v, causal=False, scale=None)`` - dense [B, N, H, d];
 * ``fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, ...)`` -
   packed ragged [T, H, d];
+* ``fwd_paged(q, k_pool, v_pool, cu_seqlens_q, page_table, seq_lens, ...)`` -
+  chunked prefill against a paged K/V cache;
 * ``decode_paged(q, k_pool, v_pool, page_table, seq_lens, ...)`` - one token
-  per sequence against a paged K/V cache.
+  per sequence against a paged K/V cache;
+* ``decode_cascade(q, k_pool, v_pool, prefix_pages, prefix_len, ...)`` - one
+  token per sequence, the sequences sharing one cached prefix;
+* ``kv_append(k_new, v_new, k_pool, v_pool, cu_new, page_table, ...)`` -
+  write new tokens' K/V rows into the paged cache.
 
 PyTorch only allocates device memory and supplies the stream; the arithmetic
 runs in the library's kernels. There is no CPU or PyTorch fallback: on a
-machine without the built library every call raises.
+machine without the built library every call raises. The device arrays'
+contents (cu_seqlens, page tables, lengths) are preconditions the library
+does not check; shapes, dtypes, devices and the head dimension of every
+tensor are checked here before the call.
 """
 from __future__ import annotations
 
@@ -22,8 +31,8 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["fwd", "fwd_varlen", "decode_paged", "decode_workspace_size", "FaError",
-           "default_scale"]
+__all__ = ["fwd", "fwd_varlen", "fwd_paged", "decode_paged", "decode_cascade", "kv_append",
+           "decode_workspace_size", "FaError", "default_scale"]
 
 _DT = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
 
@@ -55,6 +64,26 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _outputs(q: torch.Tensor, out, lse, lse_shape):
+    """O (like q) and LSE (float32, lse_shape): the caller's, checked, or new."""
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty(lse_shape, dtype=torch.float32, device=q.device) if lse is None else lse
+    _dev_tensor(o, "out")
+    _dev_tensor(l, "lse")
+    _need(o.shape == q.shape and o.dtype == q.dtype and o.device == q.device, "bad out")
+    _need(tuple(l.shape) == tuple(lse_shape) and l.dtype == torch.float32
+          and l.device == q.device, "bad lse")
+    return o, l
+
+
+def _workspace(workspace, need: int, device):
+    if workspace is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    _dev_tensor(workspace, "workspace")
+    _need(workspace.device == device, "workspace must be on the device of q")
+    return workspace
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         scale: float | None = None, out: torch.Tensor | None = None,
         lse: torch.Tensor | None = None):
@@ -68,12 +97,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     B, Nq, Hq, d = q.shape
     _, Nk, Hkv, dk = k.shape
     _need(k.shape[0] == B and dk == d, "k/v must match q in batch and head dim")
+    _need(k.device == q.device and v.device == q.device, "q, k, v must be on one device")
     if scale is None:
         scale = default_scale(d)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o.shape == q.shape and o.dtype == q.dtype and o.is_contiguous(), "bad out")
-    _need(l.shape == (B, Nq, Hq) and l.dtype == torch.float32 and l.is_contiguous(), "bad lse")
+    o, l = _outputs(q, out, lse, (B, Nq, Hq))
     _lib.check(lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
                           B, Nq, Nk, Hq, Hkv, d, _dtype(q), float(scale), int(bool(causal)),
                           _stream(q)))
@@ -96,12 +123,12 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: 
           "cu_seqlens must be int32")
     _need(cu_seqlens_q.shape == cu_seqlens_k.shape and cu_seqlens_q.dim() == 1, "bad cu_seqlens")
     Tq, Hq, d = q.shape
-    Tk, Hkv, _ = k.shape
+    Tk, Hkv, dk = k.shape
+    _need(dk == d, "k/v must match q in head dim")
     B = cu_seqlens_q.shape[0] - 1
     if scale is None:
         scale = default_scale(d)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o, l = _outputs(q, out, lse, (Tq, Hq))
     _lib.check(lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                  l.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
                                  B, int(max_seqlen_q), int(max_seqlen_k), Tq, Tk, Hq, Hkv, d,
@@ -126,14 +153,15 @@ def fwd_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     _need(cu_seqlens_q.dtype == torch.int32 and page_table.dtype == torch.int32
           and seq_lens.dtype == torch.int32, "indices must be int32")
     Tq, Hq, d = q.shape
-    num_pages, page_size, Hkv, _ = k_pool.shape
+    num_pages, page_size, Hkv, dk = k_pool.shape
+    _need(dk == d, "pools must match q in head dim")
+    _need(cu_seqlens_q.dim() == 1, "bad cu_seqlens_q")
     B = cu_seqlens_q.shape[0] - 1
     _need(page_table.dim() == 2 and page_table.shape[0] == B and seq_lens.shape == (B,),
           "bad index shapes")
     if scale is None:
         scale = default_scale(d)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o, l = _outputs(q, out, lse, (Tq, Hq))
     _lib.check(lib.fa_fwd_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), o.data_ptr(),
                                 l.data_ptr(), cu_seqlens_q.data_ptr(), page_table.data_ptr(),
                                 seq_lens.data_ptr(), B, int(max_seqlen_q), Tq,
@@ -161,17 +189,17 @@ def decode_cascade(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     _need(q.dtype == k_pool.dtype == v_pool.dtype, "q and pools must share a dtype")
     _need(page_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "indices must be int32")
     B, Hq, d = q.shape
-    num_pages, page_size, Hkv, _ = k_pool.shape
+    num_pages, page_size, Hkv, dk = k_pool.shape
+    _need(dk == d, "pools must match q in head dim")
+    _need(page_table.dim() == 2 and page_table.shape[0] == B and seq_lens.shape == (B,),
+          "bad index shapes")
     max_pages = page_table.shape[1]
-    _need(page_table.shape[0] == B and seq_lens.shape == (B,), "bad index shapes")
     if scale is None:
         scale = default_scale(d)
     need = int(lib.fa_decode_cascade_workspace_size(B, Hq, d, int(prefix_len), max_pages,
                                                     page_size))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    workspace = _workspace(workspace, need, q.device)
+    o, l = _outputs(q, out, lse, (B, Hq))
     pp = prefix_pages.data_ptr() if (prefix_pages is not None and prefix_len > 0) else None
     _lib.check(lib.fa_decode_cascade(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                      o.data_ptr(), l.data_ptr(), pp, int(prefix_len),
@@ -201,6 +229,7 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
     T_new, Hkv, d = k_new.shape
     num_pages, page_size, Hkv_p, d_p = k_pool.shape
     _need(Hkv_p == Hkv and d_p == d, "pool row shape differs from the new rows")
+    _need(cu_new.dim() == 1 and cu_new.shape[0] >= 2, "bad cu_new")
     B = cu_new.shape[0] - 1
     _need(page_table.dim() == 2 and page_table.shape[0] == B and seq_lens_before.shape == (B,),
           "bad index shapes")
@@ -230,16 +259,16 @@ def decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     _need(q.dtype == k_pool.dtype == v_pool.dtype, "q and pools must share a dtype")
     _need(page_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "indices must be int32")
     B, Hq, d = q.shape
-    num_pages, page_size, Hkv, _ = k_pool.shape
+    num_pages, page_size, Hkv, dk = k_pool.shape
+    _need(dk == d, "pools must match q in head dim")
+    _need(page_table.dim() == 2 and page_table.shape[0] == B and seq_lens.shape == (B,),
+          "bad index shapes")
     max_pages = page_table.shape[1]
-    _need(page_table.shape[0] == B and seq_lens.shape == (B,), "bad index shapes")
     if scale is None:
         scale = default_scale(d)
     need = int(lib.fa_decode_paged_workspace_size(B, Hq, d, max_pages, page_size, num_splits))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    workspace = _workspace(workspace, need, q.device)
+    o, l = _outputs(q, out, lse, (B, Hq))
     _lib.check(lib.fa_decode_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                    o.data_ptr(), l.data_ptr(), page_table.data_ptr(),
                                    seq_lens.data_ptr(), B, max_pages, num_pages, page_size, Hq,
