@@ -40,11 +40,21 @@ def dev_bits(t):
     return bits(t.cpu().view(torch.int16 if t.element_size() == 2 else torch.int32).numpy())
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-def test_append_bit_exact_against_oracle(dtype):
-    full = [1, 17, 16, 300, 45, 0]
-    before = [0, 16, 3, 299, 0, 0]
-    x, nk, nv, cu, lb, kb, vb = split_case(full, before, dtype, seed=70)
+@pytest.mark.parametrize("dtype,Hkv,d,n", [("bf16", 2, 128, 6), ("f16", 2, 128, 6),
+                                          ("f32", 2, 128, 6), ("bf16", 1, 64, 41),
+                                          ("f32", 8, 128, 41)])
+def test_append_bit_exact_against_oracle(dtype, Hkv, d, n):
+    """Rows of 128 B to 4 KB (one 16-byte piece per lane for up to 64 pieces,
+    more pieces per lane beyond); 6 or 41 sequences, and a token count that
+    is not a multiple of the four tokens a workgroup takes."""
+    if n == 6:
+        full = [1, 17, 16, 300, 45, 0]
+        before = [0, 16, 3, 299, 0, 0]
+    else:
+        rng = np.random.default_rng(71)
+        full = rng.integers(0, 120, n)
+        before = np.minimum(full, rng.integers(0, 60, n))
+    x, nk, nv, cu, lb, kb, vb = split_case(full, before, dtype, seed=70, Hkv=Hkv, d=d)
     print(f"[case] kv append {dtype} T_new={len(nk)}", flush=True)
     kp, vp = to_dev(kb, dtype), to_dev(vb, dtype)
     fa.kv_append(to_dev(nk, dtype), to_dev(nv, dtype), kp, vp, to_dev(cu, "i32"),
