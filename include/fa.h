@@ -15,8 +15,9 @@
  * --------------------------------
  * - All tensor pointers are DEVICE pointers on the current HIP device,
  *   allocated and owned by the caller. The library never allocates, frees
- *   or synchronises; each call enqueues one or two kernels on `stream` (a
- *   hipStream_t passed as void*, NULL = the null stream) and returns.
+ *   or synchronises (apart from the opt-in FA_DEBUG_VALIDATE check below);
+ *   each call enqueues one or two kernels on `stream` (a hipStream_t passed
+ *   as void*, NULL = the null stream) and returns.
  * - Tensors are dense and contiguous in the layouts stated per call, with
  *   the element type `dtype` (O has the type of Q). LSE is always float32.
  *   Q/K/V/O/pool pointers must be 16-byte aligned.
@@ -29,9 +30,21 @@
  *   Lq queries and Lk keys sees key j iff j <= i + (Lk - Lq). A row that sees
  *   no key gets O = 0 and LSE = -inf.
  * - Arguments are validated on the host before any HIP call; on an invalid
- *   argument nothing is launched and outputs are untouched. Index arrays
- *   that live on the device (cu_seqlens, page_table, seq_lens) are trusted:
- *   out-of-range contents are undefined behaviour.
+ *   argument nothing is launched and outputs are untouched. A pointer may be
+ *   NULL only when its tensor holds no element (e.g. q, o and lse of a
+ *   ragged call with Tq = 0, k and v with Tk = 0, k_new and v_new with
+ *   T_new = 0).
+ * - Index arrays that live on the device (cu_seqlens, page_table, seq_lens,
+ *   prefix_pages, cu_new) are trusted: out-of-range contents are undefined
+ *   behaviour. With the environment variable FA_DEBUG_VALIDATE set to a
+ *   value other than "" or "0" (read at every call), each call copies them
+ *   to the host after the work already queued on its stream, waits for that
+ *   copy, and returns FA_ERR_INVALID_ARG without launching anything when
+ *   they break the stated preconditions (cu_seqlens: cu[0] = 0,
+ *   non-decreasing, cu[B] = the token count, no query run above
+ *   max_seqlen_q; lengths within the page-table row; every page entry a
+ *   sequence uses inside the pool), or FA_ERR_HIP when the copy fails. This
+ *   is a debugging aid: it synchronises the stream.
  * - Calls keep no state between them and may be issued from several host
  *   threads; calls on different streams that write the same outputs race.
  */

@@ -3,8 +3,12 @@
 // so an invalid request launches nothing and touches no output.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
-#include <hip/hip_runtime.h>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
 
 #include "../../include/fa.h"
 #include "fa_internal.h"
@@ -26,9 +30,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
+// Shared checks of the attention calls. A tensor pointer may be null only
+// when that tensor holds no element: q/o/lse when there is no query row
+// (q_rows == false), k/v when there is no key (kv_rows == false). A null
+// pointer of an empty tensor is never dereferenced.
 fa_status check_common(const void* q, const void* k, const void* v, const void* o,
-                       const float* lse, int Hq, int Hkv, int d, fa_dtype dt, float scale) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+                       const float* lse, int Hq, int Hkv, int d, fa_dtype dt, float scale,
+                       bool q_rows = true, bool kv_rows = true) {
+  if (q_rows && (!q || !o || !lse)) return FA_ERR_INVALID_ARG;
+  if (kv_rows && (!k || !v)) return FA_ERR_INVALID_ARG;
   if (dt != FA_F32 && dt != FA_F16 && dt != FA_BF16) return FA_ERR_INVALID_ARG;
   if (Hq <= 0 || Hkv <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
@@ -52,6 +62,103 @@ fa_status run_fwd(fa::FwdParams& p, fa_dtype dt, int d, int causal, int max_q, v
   if (blocks > INT32_MAX) return FA_ERR_UNSUPPORTED;
   hipError_t e = fa::launch_fwd(p, to_dt(dt), d, causal != 0, (int)blocks, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+// ---- opt-in check of the device index arrays --------------------------
+// With FA_DEBUG_VALIDATE set to anything but "" or "0" in the environment,
+// each call first copies its device index arrays (cu_seqlens, page table,
+// lengths) to the host, ordered after the work already queued on its stream,
+// waits for the copy, and rejects contents that break the documented
+// preconditions with FA_ERR_INVALID_ARG before anything is launched. The
+// variable is read at every call. Off by default: the check synchronises the
+// stream and costs a device-to-host copy per call.
+bool debug_validate() {
+  const char* e = getenv("FA_DEBUG_VALIDATE");
+  return e != nullptr && e[0] != '\0' && strcmp(e, "0") != 0;
+}
+
+// n int32 values of a device array -> host; false when HIP reports an error.
+bool fetch(const int32_t* dev, int64_t n, std::vector<int32_t>& host, void* stream) {
+  host.assign((size_t)(n > 0 ? n : 0), 0);
+  if (n <= 0) return true;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(host.data(), dev, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+      hipSuccess)
+    return false;
+  return hipStreamSynchronize(st) == hipSuccess;
+}
+
+// cu[0] = 0, non-decreasing, cu[B] = total, and no run longer than max_len
+// (max_len < 0: no bound).
+bool cu_ok(const std::vector<int32_t>& cu, int B, int64_t total, int64_t max_len) {
+  if ((int)cu.size() != B + 1 || cu[0] != 0 || cu[B] != total) return false;
+  for (int s = 0; s < B; ++s) {
+    const int64_t len = (int64_t)cu[s + 1] - cu[s];
+    if (len < 0 || (max_len >= 0 && len > max_len)) return false;
+  }
+  return true;
+}
+
+// 0 <= len[b] <= max_pages * 16 and the entries of the first ceil(len / 16)
+// pages of row b of the table lie in [0, num_pages).
+bool pages_ok(const std::vector<int32_t>& table, const std::vector<int32_t>& lens, int B,
+              int max_pages, int num_pages) {
+  for (int b = 0; b < B; ++b) {
+    const int64_t len = lens[b];
+    if (len < 0 || len > (int64_t)max_pages * kPageSize) return false;
+    const int64_t used = (len + kPageSize - 1) / kPageSize;
+    for (int64_t i = 0; i < used; ++i) {
+      const int32_t pg = table[(size_t)b * max_pages + i];
+      if (pg < 0 || pg >= num_pages) return false;
+    }
+  }
+  return true;
+}
+
+// Result of a validation: FA_OK, FA_ERR_INVALID_ARG (bad contents) or
+// FA_ERR_HIP (the copy failed).
+fa_status validate_varlen(const int32_t* cu_q, const int32_t* cu_k, int B, int max_q, int Tq,
+                          int Tk, void* stream) {
+  std::vector<int32_t> hq, hk;
+  if (!fetch(cu_q, B + 1, hq, stream) || !fetch(cu_k, B + 1, hk, stream)) return FA_ERR_HIP;
+  return cu_ok(hq, B, Tq, max_q) && cu_ok(hk, B, Tk, -1) ? FA_OK : FA_ERR_INVALID_ARG;
+}
+
+fa_status validate_paged(const int32_t* table, const int32_t* lens, int B, int max_pages,
+                         int num_pages, void* stream, std::vector<int32_t>* lens_out = nullptr) {
+  std::vector<int32_t> ht, hl;
+  if (!fetch(table, (int64_t)B * max_pages, ht, stream) || !fetch(lens, B, hl, stream))
+    return FA_ERR_HIP;
+  if (!pages_ok(ht, hl, B, max_pages, num_pages)) return FA_ERR_INVALID_ARG;
+  if (lens_out) *lens_out = hl;
+  return FA_OK;
+}
+
+fa_status validate_chunks(const int32_t* cu_q, const int32_t* table, const int32_t* lens, int B,
+                          int max_q, int Tq, int max_pages, int num_pages, void* stream) {
+  std::vector<int32_t> hq, hl;
+  if (!fetch(cu_q, B + 1, hq, stream)) return FA_ERR_HIP;
+  if (!cu_ok(hq, B, Tq, max_q)) return FA_ERR_INVALID_ARG;
+  const fa_status st = validate_paged(table, lens, B, max_pages, num_pages, stream, &hl);
+  if (st != FA_OK) return st;
+  for (int s = 0; s < B; ++s)  // a chunk's queries are the last tokens of its sequence
+    if (hq[s + 1] - hq[s] > hl[s]) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+fa_status validate_prefix(const int32_t* prefix_pages, int prefix_len, int num_pages,
+                          void* stream) {
+  std::vector<int32_t> hp;
+  if (!fetch(prefix_pages, (prefix_len + kPageSize - 1) / kPageSize, hp, stream)) return FA_ERR_HIP;
+  for (int32_t pg : hp)
+    if (pg < 0 || pg >= num_pages) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+fa_status validate_append(const int32_t* cu_new, int B, int T_new, void* stream) {
+  std::vector<int32_t> hc;
+  if (!fetch(cu_new, B + 1, hc, stream)) return FA_ERR_HIP;
+  return cu_ok(hc, B, T_new, -1) ? FA_OK : FA_ERR_INVALID_ARG;
 }
 
 }  // namespace
@@ -92,13 +199,17 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
                         int max_seqlen_q, int max_seqlen_k, int Tq, int Tk, int Hq, int Hkv,
                         int d, fa_dtype dtype, float scale, int causal, void* stream) {
-  fa_status st = check_common(q, k, v, o, lse, Hq, Hkv, d, dtype, scale);
+  fa_status st = check_common(q, k, v, o, lse, Hq, Hkv, d, dtype, scale, Tq > 0, Tk > 0);
   if (st != FA_OK) return st;
   if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
   if (B <= 0 || Tq < 0 || Tk < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return FA_ERR_INVALID_ARG;
   if (max_seqlen_q > Tq) return FA_ERR_INVALID_ARG;
   if (Tq == 0 || max_seqlen_q == 0) return FA_OK;  // no query rows
+  if (debug_validate()) {
+    st = validate_varlen(cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, Tq, Tk, stream);
+    if (st != FA_OK) return st;
+  }
   fa::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
@@ -115,7 +226,7 @@ fa_status fa_fwd_paged(const void* q, const void* k_pool, const void* v_pool, vo
                        const int32_t* seq_lens, int B, int max_seqlen_q, int Tq, int max_pages,
                        int num_pages, int page_size, int Hq, int Hkv, int d, fa_dtype dtype,
                        float scale, int causal, void* stream) {
-  fa_status st = check_common(q, k_pool, v_pool, o, lse, Hq, Hkv, d, dtype, scale);
+  fa_status st = check_common(q, k_pool, v_pool, o, lse, Hq, Hkv, d, dtype, scale, Tq > 0);
   if (st != FA_OK) return st;
   if (!cu_seqlens_q || !page_table || !seq_lens) return FA_ERR_INVALID_ARG;
   if (B <= 0 || Tq < 0 || max_seqlen_q < 0 || max_seqlen_q > Tq) return FA_ERR_INVALID_ARG;
@@ -125,6 +236,11 @@ fa_status fa_fwd_paged(const void* q, const void* k_pool, const void* v_pool, vo
   if (max_pages > fa::kFwdPagedMaxPages) return FA_ERR_UNSUPPORTED;
   if ((int64_t)num_pages * kPageSize > INT32_MAX) return FA_ERR_UNSUPPORTED;
   if (Tq == 0 || max_seqlen_q == 0) return FA_OK;  // no query rows
+  if (debug_validate()) {
+    st = validate_chunks(cu_seqlens_q, page_table, seq_lens, B, max_seqlen_q, Tq, max_pages,
+                         num_pages, stream);
+    if (st != FA_OK) return st;
+  }
   fa::FwdParams p{};
   p.q = q; p.k = k_pool; p.v = v_pool; p.o = o; p.lse = lse;
   p.cu_q = cu_seqlens_q; p.cu_k = nullptr;
@@ -182,6 +298,10 @@ fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
   const int splits = (max_pages + pps - 1) / pps;
   if (B > 65535) return FA_ERR_UNSUPPORTED;  // grid y of the split merge
   if ((int64_t)B * splits * Hq > INT32_MAX) return FA_ERR_UNSUPPORTED;  // work items
+  if (debug_validate()) {
+    st = validate_paged(page_table, seq_lens, B, max_pages, num_pages, stream);
+    if (st != FA_OK) return st;
+  }
 
   fa::DecodeParams p{};
   p.q = q; p.k_pool = k_pool; p.v_pool = v_pool; p.o = o; p.lse = lse;
@@ -235,6 +355,11 @@ fa_status fa_decode_cascade(const void* q, const void* k_pool, const void* v_poo
   cascade_splits(prefix_len, max_pages, s_pre, s_suf);
   if (B > 65535) return FA_ERR_UNSUPPORTED;  // grid y of the split merge
   if ((int64_t)B * (s_pre + s_suf) * Hq > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (debug_validate()) {
+    st = validate_prefix(prefix_pages, prefix_len, num_pages, stream);
+    if (st == FA_OK) st = validate_paged(page_table, seq_lens, B, max_pages, num_pages, stream);
+    if (st != FA_OK) return st;
+  }
 
   fa::DecodeParams p{};
   p.q = q; p.k_pool = k_pool; p.v_pool = v_pool; p.o = o; p.lse = lse;
@@ -259,7 +384,9 @@ fa_status fa_kv_append(const void* k_new, const void* v_new, void* k_pool, void*
                        const int32_t* cu_new, const int32_t* page_table,
                        const int32_t* seq_lens_before, int B, int T_new, int max_pages,
                        int num_pages, int page_size, int Hkv, int d, fa_dtype dtype, void* stream) {
-  if (!k_new || !v_new || !k_pool || !v_pool || !cu_new || !page_table || !seq_lens_before)
+  // k_new / v_new hold T_new rows and may be null when T_new == 0
+  if ((T_new > 0 && (!k_new || !v_new)) || !k_pool || !v_pool || !cu_new || !page_table ||
+      !seq_lens_before)
     return FA_ERR_INVALID_ARG;
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (B <= 0 || T_new < 0 || max_pages <= 0 || num_pages <= 0 || page_size <= 0 || Hkv <= 0 ||
@@ -270,6 +397,10 @@ fa_status fa_kv_append(const void* k_new, const void* v_new, void* k_pool, void*
   if (page_size != kPageSize) return FA_ERR_UNSUPPORTED;
   if (!head_dim_ok(d)) return FA_ERR_UNSUPPORTED;
   if (T_new == 0) return FA_OK;
+  if (debug_validate()) {
+    const fa_status st = validate_append(cu_new, B, T_new, stream);
+    if (st != FA_OK) return st;
+  }
   fa::AppendParams p{};
   p.k_new = k_new; p.v_new = v_new; p.k_pool = k_pool; p.v_pool = v_pool;
   p.cu_new = cu_new; p.page_table = page_table; p.seq_lens_before = seq_lens_before;

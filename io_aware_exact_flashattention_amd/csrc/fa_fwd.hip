@@ -10,7 +10,7 @@
 //
 // gfx950 mapping of the 16-bit path (fwd_mfma_kernel):
 //  * A workgroup owns a 256-row Q tile: 8 wavefronts x 32 query rows, two
-//    per SIMD; K/V tiles of 128 keys (64 as a compile-time option).
+//    per SIMD; K/V tiles of 128 keys.
 //  * Scores are formed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_{bf16,f16}: the Q fragment is the B operand held in
 //    VGPRs for the whole loop, K rows come from LDS as the A operand. In the
@@ -23,8 +23,8 @@
 //    round-to-nearest conversion to 16 bits, without leaving the lane. The
 //    V^T operand is read from the row-major V tile with ds_read_b64_tr_b16.
 //  * K and V tiles reach LDS by direct-to-LDS global loads (no register
-//    round trip) into two rings (2 slots each with 128-key tiles, 3 with
-//    64-key tiles), issued at least two phases before they are first read.
+//    round trip) into two 2-slot rings, issued at least two phases before
+//    they are first read.
 //    A tile whose rows all lie inside the sequence is addressed from a
 //    wave-uniform base plus a 32-bit lane offset. LDS rows are XOR-swizzled
 //    in 16-byte chunks so that the rows read by one MFMA operand fall in
@@ -55,19 +55,12 @@ namespace fa {
 namespace {
 
 constexpr int kBM = 256;      // query rows per workgroup, 16-bit path (8 waves x 32)
-#ifndef FA_KBN
-#define FA_KBN 128
-#endif
-constexpr int kBN = FA_KBN;   // keys per K/V tile, 16-bit path (64 or 128)
+constexpr int kBN = 128;      // keys per K/V tile, 16-bit path
 constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
-constexpr int kKStages = kBN == 64 ? 3 : 2;  // LDS ring of K tiles
-constexpr int kVStages = kBN == 64 ? 3 : 2;  // LDS ring of V tiles
+constexpr int kKStages = 2;   // LDS ring of K tiles
+constexpr int kVStages = 2;   // LDS ring of V tiles
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maximum.
 constexpr int kWaitVmcnt0 = 0x0F70;
-// s_waitcnt immediate: vmcnt(n) (n < 64; bits 3:0 and 15:14), expcnt and
-// lgkmcnt at their maximum.
-constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // Rescale threshold of the running max (log2 units): weights stay <= 2^8.
 constexpr float kRescale = 8.f;
 
@@ -513,40 +506,22 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   __syncthreads();
   if (grp == 0) scores0();
 
-  // Barrier k opens slot k. In issue order the loads are V tile m (at
-  // barrier 2m-2, the prologue for m = 0), K tile m+1 (barrier 2m-1, the
-  // prologue for m = 0), V tile m+1 (barrier 2m).
-  // Barrier 2m+1 waits for K tile m+1 and V tile m, read by the matrix
-  // phases of slots 2m+1 and 2m+2; only V tile m+1 may still be in flight.
-  // It then issues K tile m+2 into the slot of K tile m-1, last read in
-  // slot 2m-2. Barrier 2m waits for nothing (slot 2m reads tiles that
-  // barrier 2m-1 awaited) and issues V tile m+1 into the slot of V tile
-  // m-2, last read in slot 2m-2.
+  // Barrier k opens slot k. The prologue issued K tiles 0, 1 and V tile 0;
+  // barrier 2m+1 issues K tile m+2 and V tile m+1. Slot 2m+1 (group 0's
+  // matrix phase of tile m) and slot 2m+2 (group 1's) read V tile m and K
+  // tile m+1, which barrier 2m+1 awaits; even barriers issue nothing.
   auto barrier = [&](int k) {
     const int m = k >> 1;
-    if constexpr (kKStages == 3) {
-      if ((k & 1) == 0) {
-        __syncthreads();
-        if (m + 1 < n_kv) issue_v(m + 1);
-      } else {
-        if (m + 1 < n_kv) __builtin_amdgcn_s_waitcnt(wait_vmcnt(LD));
-        else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __syncthreads();
-        if (m + 2 < n_kv) issue_k(m + 2);
-      }
+    // Barrier 2m+1 waits for everything in flight (K tile m+1 and V tile m,
+    // issued at barrier 2m-1) and issues K tile m+2 and V tile m+1 into the
+    // slots of K tile m and V tile m-1, both last read in slot 2m.
+    if ((k & 1) == 0) {
+      __syncthreads();
     } else {
-      // two-slot rings: barrier 2m+1 waits for everything in flight (K tile
-      // m+1 and V tile m, issued at barrier 2m-1) and issues K tile m+2 and
-      // V tile m+1 into the slots of K tile m and V tile m-1, both last
-      // read in slot 2m
-      if ((k & 1) == 0) {
-        __syncthreads();
-      } else {
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __syncthreads();
-        if (m + 2 < n_kv) issue_k(m + 2);
-        if (m + 1 < n_kv) issue_v(m + 1);
-      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      if (m + 2 < n_kv) issue_k(m + 2);
+      if (m + 1 < n_kv) issue_v(m + 1);
     }
   };
   // Each group runs its own loop; both pass barriers 0 .. 2 n_kv in order.

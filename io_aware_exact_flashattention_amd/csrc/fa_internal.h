@@ -2,7 +2,7 @@
 // (fa_api.cpp) and the kernel translation units.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace fa {
