@@ -10,6 +10,13 @@ the decode line reports KV bytes read per second. Each call is timed with
 HIP events on the stream it is launched on; ``ms_per_step`` is the wall
 time of the timed steps divided by their number.
 
+After the timed steps, the outputs of the last timed calls are checked
+against the fp64 oracle: the prefill on every head at four rows of every
+256-row query tile (each row's full score row), the decode on every sequence
+and query head. The errors, tolerances and a pass flag go into the JSON line
+(``parity``); a failed check makes the run exit with status 1 after printing
+it.
+
 The CPU baseline is the fp64 oracle run on a bounded sample of the same
 prefill workload (whole heads, every row) on this host's cores.
 
@@ -83,17 +90,34 @@ def measured_traffic(which: str):
     return None
 
 
-def cpu_baseline(x, heads: int):
-    """fp64 oracle on `heads` whole heads of the prefill workload."""
-    import numpy as np
-
-    import fa_inputs as fi
-    import oracle
+def host_info():
+    """CPU model, core count and the BLAS library NumPy's products run on."""
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = None, None
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')}"
+                threads = int(i.get("num_threads", 1))
+                break
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        pass
+    return {"cpu_model": model, "host_cores": os.cpu_count(), "blas": blas, "blas_threads": threads}
+
+
+def cpu_baseline(x, heads: int):
+    """fp64 oracle on `heads` whole heads of the prefill workload."""
+    import fa_inputs as fi
+    import oracle
+    info = host_info()
     B, Nq, Nk, Hq, Hkv, d = x.shape
     t0 = time.perf_counter()
     for h in range(heads):
@@ -103,9 +127,88 @@ def cpu_baseline(x, heads: int):
         oracle.attention_head(qh, kh, vh, x.scale, True)
     dt = time.perf_counter() - t0
     flops = fi.prefill_flops([Nq], [Nk], heads, d, True)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s",
+            "cores": int(info["blas_threads"] or 1), "kind": "oracle",
             "sample": f"{heads} of 32 heads of the causal N=16384 d=128 prefill, all rows, "
-                      f"fp64 NumPy, {dt:.1f} s"}
+                      f"fp64 NumPy (matrix products on {info['blas_threads']} BLAS threads, "
+                      f"element-wise passes on one), {dt:.1f} s",
+            "seconds": dt, **info}
+
+
+def device_info():
+    """CU count and engine clock of the GPU as rocminfo reports them."""
+    import subprocess
+
+    import torch
+    prop = torch.cuda.get_device_properties(0)
+    out = {"name": prop.name, "arch": getattr(prop, "gcnArchName", None),
+           "compute_units": prop.multi_processor_count, "max_clock_mhz": None}
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        agent = txt.split("gfx950", 1)[1] if "gfx950" in txt else ""
+        for ln in agent.splitlines():
+            if "Max Clock Freq" in ln:
+                out["max_clock_mhz"] = int(ln.split(":", 1)[1].split()[0])
+                break
+    except Exception:  # pragma: no cover
+        pass
+    if out["max_clock_mhz"]:
+        # dense 16-bit MFMA: 4096 flop per clock per CU (32x32x16 in 32 clocks per SIMD)
+        out["bf16_peak_from_clock_tflops"] = (out["compute_units"] * 4096 *
+                                              out["max_clock_mhz"] * 1e6 / 1e12)
+    return out
+
+
+def check_prefill(x, o, lse):
+    """Oracle on every head at four rows of each 256-row query tile (the
+    first and last row of the tile and two seeded ones); each row's full
+    score row is formed."""
+    import numpy as np
+
+    import fa_inputs as fi
+    from tests import full_oracle
+    from tests.util import LSE_TOL, O_TOL, lse_error, o_error, to_f64
+    B, Nq, Nk, Hq, Hkv, d = x.shape
+    rng = np.random.default_rng(2024)
+    rows = []
+    for t0 in range(0, Nq, 256):
+        t1 = min(Nq, t0 + 256)
+        rows += [t0, t1 - 1] + rng.integers(t0, t1, 2).tolist()
+    rows = np.unique(rows)
+    O, L = full_oracle.dense_heads(x, range(Hq), rows=rows)
+    og = to_f64(o[0, torch_index(rows, o.device)])
+    lg = to_f64(lse[0, torch_index(rows, o.device)])
+    eo = o_error(og, O, np.array([np.abs(fi.to_f64(x.v, "bf16")).max()]))
+    el = lse_error(lg, L)
+    return {"err_O": eo, "err_LSE": el, "tol_O": O_TOL["bf16"], "tol_LSE": LSE_TOL["bf16"],
+            "finite": bool(np.isfinite(og).all()),
+            "pass": bool(eo <= O_TOL["bf16"] and el <= LSE_TOL["bf16"] and np.isfinite(og).all()),
+            "checked": f"all {Hq} heads x {len(rows)} of {Nq} rows (4 per 256-row query tile)"}
+
+
+def torch_index(rows, device):
+    import torch
+    return torch.as_tensor(rows, dtype=torch.long, device=device)
+
+
+def check_decode(p, o, lse):
+    """Oracle on every sequence and query head, fed each sequence's
+    contiguous K/V (no page table)."""
+    import numpy as np
+
+    import fa_inputs as fi
+    from tests import full_oracle
+    from tests.util import LSE_TOL, O_TOL, lse_error, o_error, to_f64
+    seq = lambda src: (lambda b: src[p.cu_k[b]:p.cu_k[b + 1]])
+    O, L = full_oracle.decode_all(p.q, seq(p.k_seq), seq(p.v_seq), "bf16", p.scale)
+    og, lg = to_f64(o), to_f64(lse)
+    eo = o_error(og, O, np.array([np.abs(fi.to_f64(p.v_seq, "bf16")).max()]))
+    el = lse_error(lg, L)
+    B, Hq, _ = p.q.shape
+    return {"err_O": eo, "err_LSE": el, "tol_O": O_TOL["bf16"], "tol_LSE": LSE_TOL["bf16"],
+            "finite": bool(np.isfinite(og).all()),
+            "pass": bool(eo <= O_TOL["bf16"] and el <= LSE_TOL["bf16"] and np.isfinite(og).all()),
+            "checked": f"all {B} sequences x {Hq} query heads"}
 
 
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector, published
@@ -231,7 +334,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip the oracle check of the timed outputs (profiling runs)")
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the throughput report of the other parity workloads")
@@ -276,7 +381,6 @@ def main():
                          device=dev)
         do_ = torch.empty_like(dq)
         dl = torch.empty((Bd, Hqd), dtype=torch.float32, device=dev)
-        del p.k_seq, p.v_seq
 
     stream = torch.cuda.current_stream(dev)
 
@@ -293,6 +397,19 @@ def main():
             fa.decode_paged(dq, dkp, dvp, dpt, dsl, scale=p.scale, workspace=ws, out=do_, lse=dl)
             if ev is not None:
                 ev[3].record(stream)
+
+    # the first call of each entry point in this process (kernel code loaded
+    # on first launch), timed alone
+    torch.cuda.synchronize()
+    cold_ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    t_cold = time.perf_counter()
+    step(cold_ev)
+    torch.cuda.synchronize()
+    cold = {"wall_ms": (time.perf_counter() - t_cold) * 1e3}
+    if do_pre:
+        cold["prefill_ms"] = cold_ev[0].elapsed_time(cold_ev[1])
+    if do_dec:
+        cold["decode_ms"] = cold_ev[2].elapsed_time(cold_ev[3])
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -328,6 +445,8 @@ def main():
                         "64 seqs KV U[512,32768] seed 4, page 16, Hq=32 Hkv=8 d=128 (fa_decode_paged)",
             "prefill": {"B": B, "N": Nq, "H": Hq, "d": d, "causal": True, "flops_per_call": pre_flops},
         },
+        "cold_first_call": cold,
+        "device": device_info(),
     }
     if do_pre:
         avg = float(np.mean(pre_ms))
@@ -351,6 +470,20 @@ def main():
                          "traffic": tr_dec["bytes_per_call"] if tr_dec else None,
                          "kernel": "decode_split_kernel + decode_combine_kernel"},
         }
+    parity_ok = True
+    if not args.no_check:
+        out["parity"] = {}
+        if do_pre:
+            log("[bench] checking the timed prefill output against the oracle")
+            out["parity"]["prefill"] = check_prefill(x, o, lse)
+            parity_ok &= out["parity"]["prefill"]["pass"]
+        if do_dec:
+            log("[bench] checking the timed decode output against the oracle")
+            out["parity"]["decode"] = check_decode(p, do_, dl)
+            parity_ok &= out["parity"]["decode"]["pass"]
+        out["parity"]["pass"] = bool(parity_ok)
+    if do_dec:
+        del p.k_seq, p.v_seq
     if not args.no_other:
         log("[bench] other workloads")
         out["other_configs"] = other_configs(torch, fa, fi, to_dev, dev)
@@ -367,6 +500,9 @@ def main():
         log("[bench] cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_heads)
     print(json.dumps(out), flush=True)
+    if not parity_ok:
+        log("[bench] the timed outputs do not match the oracle")
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -6,6 +6,7 @@ import pytest
 
 import fa_inputs as fi
 import oracle
+from tests import full_oracle
 from tests.util import assert_parity, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -87,14 +88,18 @@ def test_decode_zero_length_sequence():
     check(x, "decode with empty sequences", seqs=[1, 3])
 
 
-def test_cfg4_paged_gqa_decode_sampled():
-    """Full size: 64 sequences, 1.2M tokens in 75219 permuted pages; the
-    oracle checks a sample of sequences (all 32 heads each)."""
+def test_cfg4_paged_gqa_decode_full():
+    """Full size: 64 sequences, 1.2M tokens in 75219 permuted pages; every
+    sequence and all 32 query heads against the fp64 oracle, which reads each
+    sequence's contiguous K/V."""
     x = fi.cfg4()
-    rng = np.random.default_rng(7)
-    seqs = sorted(set([int(np.argmax(x.seq_lens)), int(np.argmin(x.seq_lens))] +
-                      rng.choice(64, 6, replace=False).tolist()))
-    check(x, "cfg4 paged GQA decode", seqs=seqs)
+    print("[case] cfg4 paged GQA decode full", flush=True)
+    o, l = run(x)
+    o, l = to_f64(o), to_f64(l)
+    seq = lambda src: (lambda b: src[x.cu_k[b]:x.cu_k[b + 1]])
+    O, L = full_oracle.decode_all(x.q, seq(x.k_seq), seq(x.v_seq), x.dtype, x.scale)
+    vmax = np.abs(fi.to_f64(x.v_seq, x.dtype)).max()
+    assert_parity(o, l, O, L, np.array([vmax]), x.dtype, "cfg4 paged GQA decode full")
 
 
 def test_page_table_permutation_and_poison_bitwise():

@@ -5,6 +5,7 @@ import pytest
 
 import fa_inputs as fi
 import oracle
+from tests import full_oracle
 from tests.util import assert_parity, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -92,9 +93,16 @@ def test_cascade_matches_decode_over_aliased_page_tables():
     check(x, "cascade vs aliased tables")
 
 
-def test_cascade_shared_prompt_batch_sampled():
-    """64 sequences sharing a 16384-token prefix, suffixes U[1, 2048]."""
+def test_cascade_shared_prompt_batch_full():
+    """64 sequences sharing a 16384-token prefix, suffixes U[1, 2048]: every
+    sequence and query head against the fp64 oracle over prefix + suffix."""
     rng = np.random.default_rng(83)
     suf = rng.integers(1, 2048, 64, endpoint=True)
     x = fi.cascade(16384, suf, 32, 8, 128, "bf16", seed=83)
-    check(x, "cascade shared prompt", seqs=[0, 7, 31, 63])
+    print("[case] cascade shared prompt full", flush=True)
+    o, l = run(x)
+    o, l = to_f64(o), to_f64(l)
+    O, L = full_oracle.decode_all(x.q, lambda b: x.keys(b, "k"), lambda b: x.keys(b, "v"), "bf16",
+                                  x.pool.scale)
+    vmax = np.abs(fi.to_f64(x.pool.v_seq, "bf16")).max()
+    assert_parity(o, l, O, L, np.array([vmax]), "bf16", "cascade shared prompt full")

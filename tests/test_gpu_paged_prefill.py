@@ -6,6 +6,7 @@ import pytest
 
 import fa_inputs as fi
 import oracle
+from tests import full_oracle
 from tests.util import assert_parity, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -59,29 +60,20 @@ def test_paged_prefill_non_causal():
     check(x, "paged prefill non-causal", causal=False)
 
 
-def test_chunked_prefill_batch_sampled():
-    """16 sequences: cached prefix U[0,8192] + chunk U[1,2048]; the oracle
-    checks sampled rows of three heads of every chunk."""
+def test_chunked_prefill_batch_full():
+    """16 sequences: cached prefix U[0,8192] + chunk U[1,2048]; every row of
+    every query head of every chunk against the fp64 oracle on the
+    contiguous keys."""
     lq, lk = fi.chunked_prefill_lengths()
     x = fi.paged_prefill(lq, lk, 32, 8, 128, "bf16", seed=5)
-    print(f"[case] chunked prefill batch Tq={len(x.q)} keys={int(lk.sum())}", flush=True)
+    print(f"[case] chunked prefill batch full Tq={len(x.q)} keys={int(lk.sum())}", flush=True)
     o, l = run(x)
     o, l = to_f64(o), to_f64(l)
     assert np.all(np.isfinite(o))
     kv = x.kv
-    rng = np.random.default_rng(98)
+    O, L = full_oracle.varlen_all(x.q, kv.k_seq, kv.v_seq, x.cu_q, kv.cu_k, "bf16", kv.scale, True)
     vmax = np.abs(fi.to_f64(kv.v_seq, "bf16")).max()
-    for s in range(len(lq)):
-        a, b = int(x.cu_q[s]), int(x.cu_q[s + 1])
-        c, e = int(kv.cu_k[s]), int(kv.cu_k[s + 1])
-        rows = np.unique(np.concatenate([[0, b - a - 1], rng.integers(0, b - a, 6)]))
-        for h in (0, 17, 31):
-            g = oracle.kv_head_of(h, 32, 8)
-            O, L = oracle.attention_rows(fi.to_f64(x.q[a + rows, h], "bf16"), rows, b - a,
-                                         fi.to_f64(kv.k_seq[c:e, g], "bf16"),
-                                         fi.to_f64(kv.v_seq[c:e, g], "bf16"), kv.scale, True)
-            assert_parity(o[a + rows, h], l[a + rows, h], O, L, np.array([vmax]), "bf16",
-                          f"chunked prefill seq {s} head {h}")
+    assert_parity(o, l, O, L, np.array([vmax]), "bf16", "chunked prefill batch full")
 
 
 def test_paged_equals_contiguous_varlen_bitwise():

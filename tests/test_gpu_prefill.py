@@ -6,6 +6,7 @@ import pytest
 
 import fa_inputs as fi
 import oracle
+from tests import full_oracle
 from tests.util import assert_parity, dense_dev, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -51,24 +52,27 @@ def test_cfg1_causal_multihead(dtype, q_mult):
     check_dense_full(x, f"cfg1 {dtype} qx{q_mult:g}")
 
 
-def test_cfg2_long_context_sampled_rows():
-    """Full size B=1 H=32 N=16384 d=128 causal bf16: oracle on sampled rows
-    (each row's full score row), in the launch configuration of the bench."""
+@pytest.fixture(scope="module")
+def cfg2_run():
+    """Full size B=1 H=32 N=16384 d=128 causal bf16, in the launch
+    configuration of the bench: inputs and the GPU's O, LSE (computed once)."""
     x = fi.cfg2()
-    print(f"[case] cfg2 sampled rows", flush=True)
+    print("[case] cfg2 full: GPU call", flush=True)
     o, l = run_dense(x)
-    rng = np.random.default_rng(1234)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 16383], rng.integers(0, 16384, 27)]))
-    heads = [0, 7, 19, 31]
-    errs = []
-    vmax = np.abs(fi.to_f64(x.v, "bf16")).max()
-    for h in heads:
-        kh = fi.to_f64(x.k[0, :, h], "bf16")
-        vh = fi.to_f64(x.v[0, :, h], "bf16")
-        O, L = oracle.attention_rows(fi.to_f64(x.q[0, rows, h], "bf16"), rows, 16384, kh, vh,
-                                     x.scale, True)
-        assert_parity(o[0, rows, h], l[0, rows, h], O, L, np.array([vmax]), "bf16", f"cfg2 head {h}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    return x, o, l, np.abs(fi.to_f64(x.v, "bf16")).max()
+
+
+@pytest.mark.parametrize("h0", [0, 8, 16, 24])
+def test_cfg2_full_every_row(cfg2_run, h0):
+    """Every row of heads h0 .. h0+7 of the full-size causal prefill against
+    the fp64 oracle, element by element (the four cases cover all 32 heads)."""
+    x, o, l, vmax = cfg2_run
+    heads = list(range(h0, h0 + 8))
+    print(f"[case] cfg2 full: oracle of heads {h0}..{h0 + 7}, all 16384 rows", flush=True)
+    O, L = full_oracle.dense_heads(x, heads)
+    assert_parity(o[0][:, heads], l[0][:, heads], O, L, np.array([vmax]), "bf16",
+                  f"cfg2 full heads {h0}-{h0 + 7}")
 
 
 def test_cfg2_closed_form_zero_q():
@@ -88,7 +92,7 @@ def test_cfg2_closed_form_zero_q():
     assert err <= 1e-2 and lerr <= 1e-4 * np.log(16384)
 
 
-def check_varlen(x: fi.Varlen, what, sample_rows=None):
+def check_varlen(x: fi.Varlen, what):
     print(f"[case] {what}", flush=True)
     q, k, v = to_dev(x.q, x.dtype), to_dev(x.k, x.dtype), to_dev(x.v, x.dtype)
     cq, ck = to_dev(x.cu_q, "i32"), to_dev(x.cu_k, "i32")
@@ -96,25 +100,8 @@ def check_varlen(x: fi.Varlen, what, sample_rows=None):
     torch.cuda.synchronize()
     o, l = to_f64(o), to_f64(l)
     assert np.all(np.isfinite(o))
-    if sample_rows is None:
-        O, L = oracle.attention_varlen(fi.to_f64(x.q, x.dtype), fi.to_f64(x.k, x.dtype),
-                                       fi.to_f64(x.v, x.dtype), x.cu_q, x.cu_k, x.scale, x.causal)
-        return assert_parity(o, l, O, L, fi.to_f64(x.v, x.dtype), x.dtype, what)
-    rng = np.random.default_rng(99)
-    Hq, Hkv = x.q.shape[1], x.k.shape[1]
-    vmax = np.abs(fi.to_f64(x.v, x.dtype)).max()
-    for s in range(len(x.cu_q) - 1):
-        a, b, c, e = (int(t) for t in (x.cu_q[s], x.cu_q[s + 1], x.cu_k[s], x.cu_k[s + 1]))
-        if b == a:
-            continue
-        rows = np.unique(np.concatenate([[0, b - a - 1], rng.integers(0, b - a, sample_rows)]))
-        for h in (0, Hq // 2 + 1, Hq - 1):
-            g = oracle.kv_head_of(h, Hq, Hkv)
-            O, L = oracle.attention_rows(fi.to_f64(x.q[a + rows, h], x.dtype), rows, b - a,
-                                         fi.to_f64(x.k[c:e, g], x.dtype),
-                                         fi.to_f64(x.v[c:e, g], x.dtype), x.scale, x.causal)
-            assert_parity(o[a + rows, h], l[a + rows, h], O, L, np.array([vmax]), x.dtype,
-                          f"{what} seq {s} head {h}")
+    O, L = full_oracle.varlen_all(x.q, x.k, x.v, x.cu_q, x.cu_k, x.dtype, x.scale, x.causal)
+    return assert_parity(o, l, O, L, fi.to_f64(x.v, x.dtype), x.dtype, what)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
@@ -126,8 +113,10 @@ def test_varlen_small_with_empty_sequences(dtype, causal):
     check_varlen(x, f"varlen small {dtype} causal={causal}")
 
 
-def test_cfg3_varlen_gqa_sampled():
-    check_varlen(fi.cfg3(), "cfg3 varlen GQA", sample_rows=24)
+def test_cfg3_varlen_gqa_full():
+    """Full size: every row of every one of the 32 query heads of the 8
+    ragged sequences (15892 tokens, 8 KV heads)."""
+    check_varlen(fi.cfg3(), "cfg3 varlen GQA full")
 
 
 # ------------------------------------------------------------ bitwise --
