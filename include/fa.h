@@ -62,7 +62,9 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad scale, Hq % Hkv != 0, small workspace */
   FA_ERR_UNSUPPORTED = 2, /* valid request outside what is built: d, page size, dtype for a call */
-  FA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+  FA_ERR_HIP = 3,         /* the HIP runtime reported an error at launch */
+  FA_ERR_NO_SPACE = 4     /* fa_decode_paged_noalloc: the request needs more workspace than
+                             its fixed device buffer holds */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
@@ -170,6 +172,33 @@ fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                           int max_pages, int num_pages, int page_size, int Hq, int Hkv, int d,
                           fa_dtype dtype, float scale, int num_splits, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_paged_noalloc - fa_decode_paged without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. It computes
+ * exactly what fa_decode_paged computes with the same kernels (bitwise the
+ * same outputs), with its split partials in a fixed device buffer of
+ * FA_DECODE_NOALLOC_MAX_WORKSPACE bytes that the library holds on every GPU
+ * it runs on until the process ends. The call itself allocates nothing.
+ *   Arguments, layouts and errors as for fa_decode_paged, plus
+ *   FA_ERR_NO_SPACE when fa_decode_paged_workspace_size(B, Hq, d, max_pages,
+ *   page_size, num_splits) exceeds FA_DECODE_NOALLOC_MAX_WORKSPACE (nothing
+ *   is launched then).
+ * The buffer's address on a device is looked up once, at the first call made
+ * with that device current (FA_ERR_HIP if that fails). Every call on a GPU
+ * shares that GPU's buffer and leaves the last call's partials in it: calls
+ * that overlap on one GPU (on different streams, or from several host
+ * threads without ordering) race and may corrupt each other's results.
+ * Calls on one stream are ordered and safe. The buffer needs no clearing:
+ * the merge pass reads only partials that the same call wrote.
+ */
+#define FA_DECODE_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+fa_status fa_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool, void* o,
+                                  float* lse, const int32_t* page_table, const int32_t* seq_lens,
+                                  int B, int max_pages, int num_pages, int page_size, int Hq,
+                                  int Hkv, int d, fa_dtype dtype, float scale, int num_splits,
+                                  void* stream);
 
 /*
  * fa_decode_cascade_workspace_size - bytes of device workspace that

@@ -10,6 +10,8 @@ current HIP stream; the attention calls return (O, LSE):
   chunked prefill against a paged K/V cache;
 * ``decode_paged(q, k_pool, v_pool, page_table, seq_lens, ...)`` - one token
   per sequence against a paged K/V cache;
+* ``decode_paged_noalloc(...)`` - the same through the entry point that
+  allocates nothing (split partials in the library's fixed device buffer);
 * ``decode_cascade(q, k_pool, v_pool, prefix_pages, prefix_len, ...)`` - one
   token per sequence, the sequences sharing one cached prefix;
 * ``kv_append(k_new, v_new, k_pool, v_pool, cu_new, page_table, ...)`` -
@@ -31,8 +33,8 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["fwd", "fwd_varlen", "fwd_paged", "decode_paged", "decode_cascade", "kv_append",
-           "decode_workspace_size", "FaError", "default_scale"]
+__all__ = ["fwd", "fwd_varlen", "fwd_paged", "decode_paged", "decode_paged_noalloc",
+           "decode_cascade", "kv_append", "decode_workspace_size", "FaError", "default_scale"]
 
 _DT = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
 
@@ -243,6 +245,44 @@ def decode_workspace_size(B: int, Hq: int, d: int, max_pages: int, page_size: in
                           num_splits: int = 0) -> int:
     return int(_lib.load().fa_decode_paged_workspace_size(B, Hq, d, max_pages, page_size,
                                                           num_splits))
+
+
+def _decode_args(q, k_pool, v_pool, page_table, seq_lens):
+    for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("page_table", page_table),
+                 ("seq_lens", seq_lens)):
+        _dev_tensor(t, n)
+    _need(q.dim() == 3 and k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "bad shapes")
+    _need(q.dtype == k_pool.dtype == v_pool.dtype, "q and pools must share a dtype")
+    _need(page_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "indices must be int32")
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv, dk = k_pool.shape
+    _need(dk == d, "pools must match q in head dim")
+    _need(page_table.dim() == 2 and page_table.shape[0] == B and seq_lens.shape == (B,),
+          "bad index shapes")
+    return B, Hq, d, num_pages, page_size, Hkv, page_table.shape[1]
+
+
+def decode_paged_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                         page_table: torch.Tensor, seq_lens: torch.Tensor, num_splits: int = 0,
+                         scale: float | None = None, out: torch.Tensor | None = None,
+                         lse: torch.Tensor | None = None):
+    """Paged decode through ``fa_decode_paged_noalloc``: the library call
+    allocates nothing (its split partials go to a fixed device buffer of
+    DECODE_NOALLOC_MAX_WORKSPACE bytes; FaError FA_ERR_NO_SPACE beyond it).
+    Pass ``out`` and ``lse`` to keep this function from allocating them.
+    Same arguments and results as ``decode_paged``."""
+    lib = _lib.load()
+    B, Hq, d, num_pages, page_size, Hkv, max_pages = _decode_args(q, k_pool, v_pool, page_table,
+                                                                  seq_lens)
+    if scale is None:
+        scale = default_scale(d)
+    o, l = _outputs(q, out, lse, (B, Hq))
+    _lib.check(lib.fa_decode_paged_noalloc(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                           o.data_ptr(), l.data_ptr(), page_table.data_ptr(),
+                                           seq_lens.data_ptr(), B, max_pages, num_pages, page_size,
+                                           Hq, Hkv, d, _dtype(q), float(scale), int(num_splits),
+                                           _stream(q)))
+    return o, l
 
 
 def decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

@@ -11,12 +11,14 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa_amd.so")
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_NO_SPACE = 0, 1, 2, 3, 4
+# bytes of the fixed device buffer behind fa_decode_paged_noalloc
+DECODE_NOALLOC_MAX_WORKSPACE = 64 << 20
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 
 EXPORTS = ("fa_status_string", "fa_version", "fa_fwd", "fa_fwd_varlen", "fa_fwd_paged",
            "fa_decode_paged_workspace_size", "fa_decode_paged", "fa_decode_cascade_workspace_size",
-           "fa_decode_cascade", "fa_kv_append")
+           "fa_decode_cascade", "fa_kv_append", "fa_decode_paged_noalloc")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
@@ -41,6 +43,9 @@ _SIGNATURES = {
     "fa_kv_append": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                              _f, _i, _vp, _sz, _vp]),
+    # the same without workspace and workspace_bytes
+    "fa_decode_paged_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                                     _i, _f, _i, _vp]),
 }
 
 _lib = None

@@ -171,6 +171,8 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration";
     case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error at launch";
+    case FA_ERR_NO_SPACE:
+      return "FA_ERR_NO_SPACE: the request needs more than the fixed scratch buffer";
   }
   return "unknown fa_status";
 }
@@ -279,30 +281,40 @@ size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_pages, int p
   return (size_t)B * Hq * splits * ((size_t)d + 1) * sizeof(float);
 }
 
-fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool, void* o,
-                          float* lse, const int32_t* page_table, const int32_t* seq_lens, int B,
-                          int max_pages, int num_pages, int page_size, int Hq, int Hkv, int d,
-                          fa_dtype dtype, float scale, int num_splits, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+// Checks shared by fa_decode_paged and fa_decode_paged_noalloc (everything
+// but the workspace); on success `need` is the workspace size in bytes.
+static fa_status check_decode(const void* q, const void* k_pool, const void* v_pool, const void* o,
+                              const float* lse, const int32_t* page_table,
+                              const int32_t* seq_lens, int B, int max_pages, int num_pages,
+                              int page_size, int Hq, int Hkv, int d, fa_dtype dtype, float scale,
+                              int num_splits, size_t& need) {
   fa_status st = check_common(q, k_pool, v_pool, o, lse, Hq, Hkv, d, dtype, scale);
   if (st != FA_OK) return st;
-  if (!page_table || !seq_lens || !workspace) return FA_ERR_INVALID_ARG;
+  if (!page_table || !seq_lens) return FA_ERR_INVALID_ARG;
   if (B <= 0 || max_pages <= 0 || num_pages <= 0 || page_size <= 0) return FA_ERR_INVALID_ARG;
   if (num_splits < 0 || num_splits > max_pages) return FA_ERR_INVALID_ARG;
-  if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
   if (page_size != kPageSize) return FA_ERR_UNSUPPORTED;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
-  const size_t need = fa_decode_paged_workspace_size(B, Hq, d, max_pages, page_size, num_splits);
-  if (need == 0 || workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  need = fa_decode_paged_workspace_size(B, Hq, d, max_pages, page_size, num_splits);
+  if (need == 0) return FA_ERR_INVALID_ARG;
   const int pps = pages_per_split(max_pages, num_splits);
   const int splits = (max_pages + pps - 1) / pps;
   if (B > 65535) return FA_ERR_UNSUPPORTED;  // grid y of the split merge
   if ((int64_t)B * splits * Hq > INT32_MAX) return FA_ERR_UNSUPPORTED;  // work items
+  return FA_OK;
+}
+
+// Launches a checked decode with its partials in `workspace`.
+static fa_status run_decode(const void* q, const void* k_pool, const void* v_pool, void* o,
+                            float* lse, const int32_t* page_table, const int32_t* seq_lens, int B,
+                            int max_pages, int num_pages, int Hq, int Hkv, int d, fa_dtype dtype,
+                            float scale, int num_splits, void* workspace, void* stream) {
   if (debug_validate()) {
-    st = validate_paged(page_table, seq_lens, B, max_pages, num_pages, stream);
+    const fa_status st = validate_paged(page_table, seq_lens, B, max_pages, num_pages, stream);
     if (st != FA_OK) return st;
   }
-
+  const int pps = pages_per_split(max_pages, num_splits);
+  const int splits = (max_pages + pps - 1) / pps;
   fa::DecodeParams p{};
   p.q = q; p.k_pool = k_pool; p.v_pool = v_pool; p.o = o; p.lse = lse;
   p.page_table = page_table; p.seq_lens = seq_lens;
@@ -315,6 +327,37 @@ fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
   p.lse_part = ws + (size_t)B * Hq * splits * d;
   hipError_t e = fa::launch_decode(p, to_dt(dtype), d, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_decode_paged(const void* q, const void* k_pool, const void* v_pool, void* o,
+                          float* lse, const int32_t* page_table, const int32_t* seq_lens, int B,
+                          int max_pages, int num_pages, int page_size, int Hq, int Hkv, int d,
+                          fa_dtype dtype, float scale, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  fa_status st = check_decode(q, k_pool, v_pool, o, lse, page_table, seq_lens, B, max_pages,
+                              num_pages, page_size, Hq, Hkv, d, dtype, scale, num_splits, need);
+  if (st != FA_OK) return st;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  return run_decode(q, k_pool, v_pool, o, lse, page_table, seq_lens, B, max_pages, num_pages, Hq,
+                    Hkv, d, dtype, scale, num_splits, workspace, stream);
+}
+
+fa_status fa_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool, void* o,
+                                  float* lse, const int32_t* page_table, const int32_t* seq_lens,
+                                  int B, int max_pages, int num_pages, int page_size, int Hq,
+                                  int Hkv, int d, fa_dtype dtype, float scale, int num_splits,
+                                  void* stream) {
+  size_t need = 0;
+  fa_status st = check_decode(q, k_pool, v_pool, o, lse, page_table, seq_lens, B, max_pages,
+                              num_pages, page_size, Hq, Hkv, d, dtype, scale, num_splits, need);
+  if (st != FA_OK) return st;
+  static_assert(fa::kDecodeScratchBytes == FA_DECODE_NOALLOC_MAX_WORKSPACE, "scratch size");
+  if (need > fa::kDecodeScratchBytes) return FA_ERR_NO_SPACE;
+  void* scratch = nullptr;
+  if (fa::decode_scratch(&scratch) != hipSuccess) return FA_ERR_HIP;
+  return run_decode(q, k_pool, v_pool, o, lse, page_table, seq_lens, B, max_pages, num_pages, Hq,
+                    Hkv, d, dtype, scale, num_splits, scratch, stream);
 }
 
 // Splits of a cascade decode: prefix splits (32 pages each) lead, then the

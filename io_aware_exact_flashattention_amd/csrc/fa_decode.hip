@@ -32,6 +32,8 @@
 // Slots of a last page beyond the sequence end never enter the result:
 // their scores are -inf and their V values are replaced by zero before use,
 // so NaN garbage there cannot leak.
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -574,6 +576,30 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+// Fixed device workspace of the allocation-free decode entry point: each GPU
+// the library runs on holds its own copy until the process ends. In host
+// code `scratch` names a host-side stand-in, never the device memory: its
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 // launch_t runs the prefix pass whenever p.prefix_len > 0.
 hipError_t launch_decode_cascade(const DecodeParams& p, Dt dt, int d, hipStream_t st) {

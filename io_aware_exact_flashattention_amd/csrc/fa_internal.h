@@ -93,4 +93,11 @@ hipError_t launch_decode_cascade(const DecodeParams& p, Dt dt, int d, hipStream_
 
 hipError_t launch_append(const AppendParams& p, int T_new, hipStream_t stream);
 
+// Bytes of the fixed device workspace behind fa_decode_paged_noalloc.
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+// Device address of that workspace on the current device (looked up once
+// per device, then cached); the memory itself lives until the process ends.
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace fa

@@ -103,6 +103,23 @@ static void check_decode() {
   CHECK(fa_decode_paged(P, P, P, P, (float*)P, (int32_t*)P, (int32_t*)P, 64, 2017, 75219, 16, 32, 8,
                         128, FA_BF16, 0.1f, 7, P, need7, nullptr) == FA_OK);
   CHECK(g_stub.dec.pages_per_split == 64 && g_stub.dec.max_splits == 32);
+
+  // the allocation-free variant: the same launch, partials in the library's buffer
+  const int lookups = g_stub.scratch_lookups;
+  CHECK(fa_decode_paged_noalloc(P, P, P, P, (float*)P, (int32_t*)P, (int32_t*)P, 64, 2017, 75219,
+                                16, 32, 8, 128, FA_BF16, 0.1f, 0, nullptr) == FA_OK);
+  CHECK(g_stub.last_kind == StubState::DECODE && g_stub.dec.pages_per_split == 48 &&
+        g_stub.dec.max_splits == 43 && g_stub.scratch_lookups == lookups + 1);
+  CHECK((char*)g_stub.dec.lse_part - (char*)g_stub.dec.o_part == (ptrdiff_t)64 * 32 * 43 * 128 * 4);
+  // a request beyond the fixed buffer: FA_ERR_NO_SPACE, nothing launched or looked up
+  const size_t big = fa_decode_paged_workspace_size(128, 64, 128, 2017, 16, 0);
+  CHECK(big > FA_DECODE_NOALLOC_MAX_WORKSPACE);
+  const int n = g_stub.launches;
+  CHECK(fa_decode_paged_noalloc(P, P, P, P, (float*)P, (int32_t*)P, (int32_t*)P, 128, 2017, 75219,
+                                16, 64, 8, 128, FA_BF16, 0.1f, 0, nullptr) == FA_ERR_NO_SPACE);
+  CHECK(fa_decode_paged_noalloc(P, P, P, P, (float*)P, (int32_t*)P, (int32_t*)P, 64, 2017, 75219,
+                                8, 32, 8, 128, FA_BF16, 0.1f, 0, nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(g_stub.launches == n && g_stub.scratch_lookups == lookups + 1);
 }
 
 static void check_append() {
@@ -208,6 +225,7 @@ static void check_validate() {
 int main() {
   CHECK(fa_version() >= 100);
   CHECK(fa_status_string((fa_status)42) != nullptr);
+  CHECK(fa_status_string(FA_ERR_NO_SPACE)[0] == 'F');
   check_fwd();
   check_varlen();
   check_decode();

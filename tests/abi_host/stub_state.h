@@ -8,6 +8,7 @@ struct StubState {
   enum Kind { NONE, FWD, FWD_PAGED, DECODE, CASCADE, APPEND };
   int launches = 0;
   int copies = 0;
+  int scratch_lookups = 0;
   bool fail_copies = false;  // make hipMemcpyAsync report an error
   Kind last_kind = NONE;
   int grid = 0;

@@ -35,9 +35,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(4):
+    for s in range(5):
         assert lib.fa_status_string(s).decode().startswith(
-            ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"][s])
+            ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
+             "FA_ERR_NO_SPACE"][s])
     assert lib.fa_version() >= 100
 
 
@@ -100,6 +101,25 @@ def decode(lib, **kw):
 ])
 def test_decode_rejects(lib, kw, expect):
     assert decode(lib, **kw) == expect
+
+
+def decode_noalloc(lib, **kw):
+    a = dict(q=P, kp=P, vp=P, o=P, lse=P, pt=P, sl=P, B=2, mp=4, npg=8, ps=16, Hq=4, Hkv=1, d=128,
+             dt=2, scale=0.1, ns=0, stream=None)
+    a.update(kw)
+    return lib.fa_decode_paged_noalloc(a["q"], a["kp"], a["vp"], a["o"], a["lse"], a["pt"], a["sl"],
+                                       a["B"], a["mp"], a["npg"], a["ps"], a["Hq"], a["Hkv"], a["d"],
+                                       a["dt"], a["scale"], a["ns"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(pt=None), 1), (dict(sl=None), 1), (dict(ns=-1), 1), (dict(ns=5), 1), (dict(mp=0), 1),
+    (dict(ps=8), 2), (dict(dt=0), 2), (dict(Hq=4, Hkv=3), 1), (dict(d=80), 2),
+    # more partials than the fixed device buffer holds: 128 x 64 heads x 43 splits x 129 floats
+    (dict(B=128, Hq=64, Hkv=8, mp=2017, npg=75219), 4),
+])
+def test_decode_noalloc_rejects(lib, kw, expect):
+    assert decode_noalloc(lib, **kw) == expect
 
 
 def test_workspace_size(lib):
