@@ -46,10 +46,16 @@ def lse_error(l_gpu, l_ref) -> float:
     return float(np.max(np.abs(l_gpu[fin] - l_ref[fin]) / np.maximum(1.0, np.abs(l_ref[fin]))))
 
 
+# (case, dtype, err_O, err_LSE) of every parity check of the session, printed
+# by the terminal summary in tests/conftest.py
+PARITY_LOG = []
+
+
 def assert_parity(o_gpu, l_gpu, o_ref, l_ref, v_read, dtype, what=""):
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite O"
     eo = o_error(o_gpu, o_ref, v_read)
     el = lse_error(l_gpu, l_ref)
+    PARITY_LOG.append((what, dtype, eo, el))
     print(f"[parity] {what}: err_O={eo:.3e} (tol {O_TOL[dtype]:.0e}) err_LSE={el:.3e} "
           f"(tol {LSE_TOL[dtype]:.0e})", flush=True)
     assert eo <= O_TOL[dtype], f"{what}: O error {eo:.3e} > {O_TOL[dtype]:.0e}"
