@@ -20,7 +20,8 @@ drawn on several threads without changing any value:
 * ``default_rng(seed)``          - structure: lengths, then the page permutation;
 * ``default_rng([seed, 1])``      - Q;
 * ``default_rng([seed, 2, c])``   - K, chunk c;
-* ``default_rng([seed, 3, c])``   - V, chunk c.
+* ``default_rng([seed, 3, c])``   - V, chunk c;
+* ``default_rng([seed, 4])``      - the output gradient dO of the backward pass.
 
 Dense tensors are drawn in chunks of whole leading rows (``_CHUNK_ROWS``
 rows of the flattened ``[rows, H, d]`` view); ragged and paged K/V are drawn
@@ -160,6 +161,14 @@ def dense(B, Nq, Nk, Hq, Hkv, d, dtype, seed, causal, q_mult=1.0, name="") -> De
     k = _draw_rows(seed, 2, B * Nk, (Hkv, d), dtype).reshape(B, Nk, Hkv, d)
     v = _draw_rows(seed, 3, B * Nk, (Hkv, d), dtype).reshape(B, Nk, Hkv, d)
     return Dense(q, k, v, dtype, causal, default_scale(d), name)
+
+
+def grad_out(shape, dtype, seed) -> np.ndarray:
+    """An output gradient dO for the backward pass: i.i.d. N(0,1) of the
+    given shape from its own stream ``default_rng([seed, 4])``, rounded to
+    the storage type."""
+    rng = np.random.default_rng([seed, 4])
+    return round_to(rng.standard_normal(shape, dtype=np.float32), dtype)
 
 
 # ----------------------------------------------------------------- varlen --

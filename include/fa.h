@@ -264,6 +264,38 @@ fa_status fa_kv_append(const void* k_new, const void* v_new, void* k_pool, void*
                        const int32_t* seq_lens_before, int B, int T_new, int max_pages,
                        int num_pages, int page_size, int Hkv, int d, fa_dtype dtype, void* stream);
 
+/*
+ * fa_bwd_workspace_size - bytes of device workspace that fa_bwd needs
+ * (one float32 per query row and head). Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_size(int B, int Nq, int Hq);
+
+/*
+ * fa_bwd - gradients of dense attention with respect to Q, K and V, given
+ * the output gradient dO and the O and LSE that fa_fwd returned for the
+ * same q, k, v, scale and mask. The pages define only the forward pass
+ * ("I/O-Aware Kernels", section "Naive attention: materializing the k x k
+ * score matrix": S = scale Q K^T, P = row softmax of S, O = P V); these are
+ * its chain-rule gradients, dV = P^T dO, dS = P o (dO V^T - rowsum(dO o O)),
+ * dQ = scale dS K, dK = scale dS^T Q, computed as in section "FlashAttention:
+ * tiling + online softmax": P is recomputed tile by tile from the saved LSE
+ * and nothing of size Nq x Nk reaches device memory. LSE is not
+ * differentiated.
+ *   q, o, dout [B, Nq, Hq, d] dtype; k, v [B, Nk, Hkv, d] dtype;
+ *   lse [B, Nq, Hq] float32 (as written by fa_fwd)
+ *   dq [B, Nq, Hq, d], dk, dv [B, Nk, Hkv, d] dtype (written): with
+ *     grouped-query heads, dk and dv of a key/value head sum the gradients
+ *     of every query head that reads it
+ *   workspace  at least fa_bwd_workspace_size(B, Nq, Hq) bytes of device
+ *     memory owned by the caller (scratch: rowsum(dO o O) per row and head)
+ * dtype FA_F16 or FA_BF16; causal masks as for fa_fwd (bottom-right). Two
+ * kernels on `stream`, deterministic (fixed summation order, no atomics).
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq,
+                 int Hkv, int d, fa_dtype dtype, float scale, int causal, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

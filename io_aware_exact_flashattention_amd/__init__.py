@@ -15,7 +15,9 @@ current HIP stream; the attention calls return (O, LSE):
 * ``decode_cascade(q, k_pool, v_pool, prefix_pages, prefix_len, ...)`` - one
   token per sequence, the sequences sharing one cached prefix;
 * ``kv_append(k_new, v_new, k_pool, v_pool, cu_new, page_table, ...)`` -
-  write new tokens' K/V rows into the paged cache.
+  write new tokens' K/V rows into the paged cache;
+* ``bwd(q, k, v, o, lse, dout, causal=False, ...)`` - gradients (dQ, dK, dV)
+  of dense attention from the forward pass's O and LSE.
 
 PyTorch only allocates device memory and supplies the stream; the arithmetic
 runs in the library's kernels. There is no CPU or PyTorch fallback: on a
@@ -34,7 +36,8 @@ from . import _lib
 from ._lib import FaError
 
 __all__ = ["fwd", "fwd_varlen", "fwd_paged", "decode_paged", "decode_paged_noalloc",
-           "decode_cascade", "kv_append", "decode_workspace_size", "FaError", "default_scale"]
+           "decode_cascade", "kv_append", "bwd", "decode_workspace_size", "FaError",
+           "default_scale"]
 
 _DT = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
 
@@ -316,3 +319,41 @@ def decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                    _stream(q)))
     return o, l
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, causal: bool = False, scale: float | None = None,
+        dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+        dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Gradients of dense attention. q, o, dout [B, Nq, Hq, d]; k, v [B, Nk,
+    Hkv, d]; lse float32 [B, Nq, Hq] as returned by ``fwd`` -> (dQ like q,
+    dK like k, dV like v)."""
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
+        _dev_tensor(t, n)
+    _need(q.dim() == 4 and k.dim() == 4 and k.shape == v.shape, "bad shapes")
+    _need(o.shape == q.shape and dout.shape == q.shape, "o and dout must be shaped like q")
+    _need(q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype, "tensors must share a dtype")
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, dk_ = k.shape
+    _need(k.shape[0] == B and dk_ == d, "k/v must match q in batch and head dim")
+    _need(tuple(lse.shape) == (B, Nq, Hq) and lse.dtype == torch.float32, "bad lse")
+    for t in (k, v, o, lse, dout):
+        _need(t.device == q.device, "tensors must be on one device")
+    if scale is None:
+        scale = default_scale(d)
+    grads = []
+    for name, g, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        g = torch.empty_like(like) if g is None else g
+        _dev_tensor(g, name)
+        _need(g.shape == like.shape and g.dtype == like.dtype and g.device == q.device,
+              f"bad {name}")
+        grads.append(g)
+    need = int(lib.fa_bwd_workspace_size(B, Nq, Hq))
+    workspace = _workspace(workspace, need, q.device)
+    _lib.check(lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                          grads[2].data_ptr(), B, Nq, Nk, Hq, Hkv, d, _dtype(q), float(scale),
+                          int(bool(causal)), workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), _stream(q)))
+    return tuple(grads)

@@ -18,7 +18,8 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 
 EXPORTS = ("fa_status_string", "fa_version", "fa_fwd", "fa_fwd_varlen", "fa_fwd_paged",
            "fa_decode_paged_workspace_size", "fa_decode_paged", "fa_decode_cascade_workspace_size",
-           "fa_decode_cascade", "fa_kv_append", "fa_decode_paged_noalloc")
+           "fa_decode_cascade", "fa_kv_append", "fa_decode_paged_noalloc", "fa_bwd_workspace_size",
+           "fa_bwd")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
@@ -43,6 +44,10 @@ _SIGNATURES = {
     "fa_kv_append": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                              _f, _i, _vp, _sz, _vp]),
+    "fa_bwd_workspace_size": (_sz, [_i, _i, _i]),
+    # q k v o lse dout dq dk dv B Nq Nk Hq Hkv d dtype scale causal workspace workspace_bytes stream
+    "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i,
+                    _vp, _sz, _vp]),
     # the same without workspace and workspace_bytes
     "fa_decode_paged_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                      _i, _f, _i, _vp]),

@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa_amd.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_cache.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_cache.hip", "fa_bwd.hip"]
 
 ARCH = "gfx950"
 COMMON = [

@@ -423,6 +423,39 @@ fa_status fa_decode_cascade(const void* q, const void* k_pool, const void* v_poo
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_bwd_workspace_size(int B, int Nq, int Hq) {
+  if (B <= 0 || Nq <= 0 || Hq <= 0) return 0;
+  return (size_t)B * Nq * Hq * sizeof(float);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq,
+                 int Hkv, int d, fa_dtype dtype, float scale, int causal, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  fa_status st = check_common(q, k, v, o, lse, Hq, Hkv, d, dtype, scale);
+  if (st != FA_OK) return st;
+  if (!dout || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID_ARG;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(workspace))
+    return FA_ERR_INVALID_ARG;
+  if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_INVALID_ARG;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Nq > INT32_MAX || (int64_t)B * Nk > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa_bwd_workspace_size(B, Nq, Hq)) return FA_ERR_INVALID_ARG;
+  if (fa::bwd_grid_blocks(B, Nq, Nk, Hq, Hkv) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  fa::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.dsum = static_cast<float*>(workspace);
+  p.B = B; p.Nq = Nq; p.Nk = Nk; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.q_row = (int64_t)Hq * d;
+  p.kv_row = (int64_t)Hkv * d;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  hipError_t e = fa::launch_bwd(p, to_dt(dtype), d, causal != 0, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                        const int32_t* cu_new, const int32_t* page_table,
                        const int32_t* seq_lens_before, int B, int T_new, int max_pages,

@@ -77,6 +77,26 @@ struct AppendParams {
   int64_t row_bytes;             // Hkv * d * element size (a multiple of 16)
 };
 
+// Gradients of dense attention (fa_bwd). q, o, dout, dq: [B, Nq, Hq, d];
+// k, v, dk, dv: [B, Nk, Hkv, d]; lse, dsum: [B, Nq, Hq] fp32.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;       // workspace: D = rowsum(dO o O) of every query row
+  int B, Nq, Nk, Hq, Hkv, group;
+  int64_t q_row;     // Hq * d
+  int64_t kv_row;    // Hkv * d
+  float scale;       // scale of the logits
+  float scale_log2;  // scale * log2(e)
+};
+
 enum class Dt { F32, F16, Bf16 };
 
 // Each launcher enqueues its kernel(s) on `stream` and returns hipGetLastError().
@@ -92,6 +112,11 @@ hipError_t launch_decode(const DecodeParams& p, Dt dt, int d, hipStream_t stream
 hipError_t launch_decode_cascade(const DecodeParams& p, Dt dt, int d, hipStream_t stream);
 
 hipError_t launch_append(const AppendParams& p, int T_new, hipStream_t stream);
+
+// Backward pass: the dQ kernel (which also writes dsum), then the dK/dV kernel.
+hipError_t launch_bwd(const BwdParams& p, Dt dt, int d, bool causal, hipStream_t stream);
+// Workgroups of the larger of the two backward launches.
+int64_t bwd_grid_blocks(int B, int Nq, int Nk, int Hq, int Hkv);
 
 // Bytes of the fixed device workspace behind fa_decode_paged_noalloc.
 constexpr size_t kDecodeScratchBytes = size_t(64) << 20;

@@ -137,6 +137,23 @@ static void check_append() {
         g_stub.grid == 3);
 }
 
+static void check_bwd() {
+  const size_t ws = fa_bwd_workspace_size(1, 16384, 32);
+  CHECK(ws == (size_t)16384 * 32 * 4);
+  auto call = [&](void* dq, size_t bytes, fa_dtype dt) {
+    return fa_bwd(P, P, P, P, (float*)P, P, dq, P, P, 1, 16384, 16384, 32, 8, 128, dt, 0.088f, 1,
+                  P, bytes, nullptr);
+  };
+  const int before = g_stub.launches;
+  CHECK(call(nullptr, ws, FA_BF16) == FA_ERR_INVALID_ARG);
+  CHECK(call(P, ws - 4, FA_BF16) == FA_ERR_INVALID_ARG);
+  CHECK(call(P, ws, FA_F32) == FA_ERR_UNSUPPORTED);
+  CHECK(g_stub.launches == before);
+  CHECK(call(P, ws, FA_BF16) == FA_OK);
+  CHECK(g_stub.last_kind == StubState::BWD && g_stub.bwd.group == 4 &&
+        g_stub.bwd.q_row == 32 * 128 && g_stub.bwd.kv_row == 8 * 128 && g_stub.bwd.dsum == P);
+}
+
 // ---- FA_DEBUG_VALIDATE: the stubbed copy reads these host arrays --------
 static void check_validate() {
   setenv("FA_DEBUG_VALIDATE", "1", 1);
@@ -230,6 +247,7 @@ int main() {
   check_varlen();
   check_decode();
   check_append();
+  check_bwd();
   check_validate();
   printf("abi_host_check: %d checks passed\n", g_checks);
   return 0;

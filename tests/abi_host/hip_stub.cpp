@@ -55,6 +55,19 @@ hipError_t launch_append(const AppendParams& p, int T_new, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t launch_bwd(const BwdParams& p, Dt, int, bool, hipStream_t) {
+  g_stub.launches++;
+  g_stub.last_kind = StubState::BWD;
+  g_stub.bwd = p;
+  return hipSuccess;
+}
+
+int64_t bwd_grid_blocks(int B, int Nq, int Nk, int Hq, int Hkv) {
+  const int64_t a = (int64_t)B * Hq * ((Nq + 127) / 128);
+  const int64_t c = (int64_t)B * Hkv * ((Nk + 127) / 128);
+  return a > c ? a : c;
+}
+
 // a fixed host buffer stands in for the library's device scratch array
 hipError_t decode_scratch(void** ptr) {
   alignas(256) static char buf[256];

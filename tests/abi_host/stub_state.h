@@ -5,7 +5,7 @@
 #include "fa_internal.h"
 
 struct StubState {
-  enum Kind { NONE, FWD, FWD_PAGED, DECODE, CASCADE, APPEND };
+  enum Kind { NONE, FWD, FWD_PAGED, DECODE, CASCADE, APPEND, BWD };
   int launches = 0;
   int copies = 0;
   int scratch_lookups = 0;
@@ -15,6 +15,7 @@ struct StubState {
   fa::FwdParams fwd{};
   fa::DecodeParams dec{};
   fa::AppendParams app{};
+  fa::BwdParams bwd{};
 };
 
 extern StubState g_stub;

@@ -201,3 +201,27 @@ def test_cascade_workspace_size(lib):
     assert f(2, 4, 128, 0, 4, 16) == 2 * 4 * 1 * 129 * 4
     assert f(1, 1, 64, 16384, 70, 16) == 1 * 1 * (32 + 9) * 65 * 4
     assert f(0, 4, 128, 1, 4, 16) == 0
+
+
+def bwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Nq=8, Nk=8, Hq=2, Hkv=1,
+             d=64, dt=2, scale=0.125, causal=1, ws=P, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                      a["B"], a["Nq"], a["Nk"], a["Hq"], a["Hkv"], a["d"], a["dt"], a["scale"],
+                      a["causal"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(do=None), 1), (dict(dq=None), 1), (dict(dk=None), 1), (dict(dv=None), 1),
+    (dict(ws=None), 1), (dict(wsb=8 * 2 * 4 - 1), 1), (dict(o=None), 1), (dict(dq=40), 1),
+    (dict(B=0), 1), (dict(Nk=0), 1), (dict(Hq=3, Hkv=2), 1), (dict(dt=0), 2), (dict(d=96), 2),
+    (dict(scale=float("nan")), 1),
+])
+def test_bwd_rejects(lib, kw, expect):
+    assert bwd(lib, **kw) == expect
+
+
+def test_bwd_workspace_size(lib):
+    assert lib.fa_bwd_workspace_size(4, 2048, 16) == 4 * 2048 * 16 * 4
+    assert lib.fa_bwd_workspace_size(0, 2048, 16) == 0
