@@ -302,6 +302,29 @@ def other_configs(torch, fa, fi, to_dev, dev, reps=20):
         "frac": moved / (a_mean * 1e-3) / 1e9 / PEAK_HBM_GBS}
     del kn, vn, cn, lb
 
+    # backward pass (fa_bwd): work = the five products of the chain rule
+    # (S, dP, dV, dK, dQ: 10 * Hq * Nq * Nk * d flops, halved when causal);
+    # the kernels recompute S and dP once more (seven products)
+    for key, x, desc in (
+            ("bwd_long_context", fi.cfg2(),
+             "fa_bwd: causal bf16 B=1 H=32 N=16384 d=128 (dQ kernel + dK/dV kernel)"),
+            ("bwd_causal_B4_H16_N2048_d64", fi.cfg1(),
+             "fa_bwd: causal bf16 B=4 H=16 N=2048 d=64 (dQ kernel + dK/dV kernel)")):
+        B, Nq, Nk, Hq, Hkv, d = x.shape
+        q, k, v = to_dev(x.q, x.dtype), to_dev(x.k, x.dtype), to_dev(x.v, x.dtype)
+        o, l = fa.fwd(q, k, v, causal=True, scale=x.scale)
+        g_out = to_dev(fi.grad_out((B, Nq, Hq, d), x.dtype, 2), x.dtype)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        wsb = torch.empty(B * Nq * Hq * 4, dtype=torch.uint8, device=dev)
+        mean, mn = timed(lambda: fa.bwd(q, k, v, o, l, g_out, causal=True, scale=x.scale, dq=dq,
+                                        dk=dk, dv=dv, workspace=wsb))
+        flops = 2.5 * fi.prefill_flops([Nq] * B, [Nk] * B, Hq, d, True)
+        tf = flops / (mean * 1e-3) / 1e12
+        res[key] = {"workload": desc, "dtype": "bf16", "ms_mean": mean, "ms_min": mn,
+                    "tflops": tf, "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS,
+                    "flops_per_call": flops}
+        del q, k, v, o, l, g_out, dq, dk, dv, wsb
+
     # shared-prompt decode: 64 sequences on one 16384-token prefix; the
     # unique K/V bytes (prefix once + suffixes) and the bytes a plain paged
     # decode would read (prefix once per sequence)
