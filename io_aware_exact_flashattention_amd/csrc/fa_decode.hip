@@ -363,8 +363,12 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB, PREFIX>()))) voi
         sc[cb][i] = ok ? acc[i] * c2 : neg_inf();
         mx[cb] = fmaxf(mx[cb], sc[cb][i]);
       }
-      mx[cb] = fmaxf(mx[cb], xor_lane(mx[cb], 16));
-      mx[cb] = fmaxf(mx[cb], xor_lane(mx[cb], 32));
+      // across the four token groups (lanes l16 + 16 j), inside the vector ALU
+      {
+        float a, b;
+        row_pair(mx[cb], a, b);
+        mx[cb] = max_halves(fmaxf(a, b));
+      }
     }
 
     if constexpr (MFMA_PV) {
@@ -436,8 +440,9 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<D, GB, PREFIX>()))) voi
 
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    l_lane[cb] += xor_lane(l_lane[cb], 16);
-    l_lane[cb] += xor_lane(l_lane[cb], 32);
+    float a, b;
+    row_pair(l_lane[cb], a, b);
+    l_lane[cb] = sum_halves(a + b);
   }
   if constexpr (MFMA_PV) {
     // lane l: query 16 cb + l16, d = 16 db + 4 j + i

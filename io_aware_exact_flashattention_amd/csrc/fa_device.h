@@ -77,6 +77,17 @@ __device__ __forceinline__ void half_pair(float x, float& a, float& b) {
   a = __builtin_bit_cast(float, r0);
   b = __builtin_bit_cast(float, r1);
 }
+// The values of lanes i and i^16, both in every lane: v_permlane16_swap
+// exchanges the odd 16-lane rows of one copy of x with the even rows of the
+// other, so every lane ends with its own value and its partner's (in either
+// order).
+__device__ __forceinline__ void row_pair(float x, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
 // max / sum of lanes i and i^32 (the same value in both lanes of a pair)
 __device__ __forceinline__ float max_halves(float x) {
   float a, b;

@@ -45,9 +45,9 @@
 //  * Causal: K/V tiles that no row of the Q tile may see are never loaded;
 //    only tiles that cross the diagonal or the sequence end are masked.
 //
-// fp32 inputs take fwd_f32_kernel: the same online softmax on the vector
-// ALUs (4 lanes per query row), for exact fp32 arithmetic, with the key
-// range of a 32-row tile shared by four groups of threads and merged.
+// fp32 inputs take fwd_f32_kernel: the same fused pass on the fp32 matrix
+// cores (v_mfma_f32_32x32x2_f32), fp32 throughout, with the key range of a
+// 32-row tile shared by four wavefronts and merged.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -566,24 +566,47 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
 }
 
 // ------------------------------------------------------------------ fp32 --
-constexpr int kBM32 = 32;     // query rows per workgroup
-constexpr int kBN32 = 32;     // keys per tile
-constexpr int kSplit32 = 4;   // key splits of a workgroup
-constexpr int kThreads32 = 128 * kSplit32;
+constexpr int kBM32 = 32;  // query rows per workgroup
+constexpr int kBN32 = 32;  // keys per tile
+// key splits of a workgroup, one wavefront each: eight at d = 64 (128 KB
+// of tiles), four at d = 128 (the same LDS)
+template <int D> constexpr int waves32() { return D == 64 ? 8 : 4; }
 
-// Exact fp32 path on the vector ALUs. A workgroup owns 32 query rows; each
-// of its kSplit32 groups of 128 threads (4 lanes per row, D/4 values of d
-// per lane) runs the online softmax over every kSplit32-th K/V tile of the
-// rows' key range, starting at its own index (so a causal range is shared
-// evenly). The groups' states (m, l, O) are then merged in a fixed order,
-// the same log-sum-exp algebra as the split merge of the decode.
+// fp32 path: both products on the fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32: A and B one float per lane, 32x32 fp32 result).
+// A workgroup owns 32 query rows; wavefront w of its W takes K/V tiles w,
+// w+W, ... of the rows' key range, runs the online softmax over them with
+// the exact running max, and the W (m, l, O) states are merged at the end
+// in a fixed order (the log-sum-exp algebra of the split merge of the
+// decode).
+//  * S^T = K Q^T as in the 16-bit kernel, a lane owning query l % 32. The
+//    contraction over d is taken in a permuted order so that one
+//    ds_read_b128 of a K row gives the A operands of four MFMA steps: step
+//    4u + i, lane half h reads d = 8u + 4h + i. The Q fragment (B) follows
+//    the same order and stays in registers.
+//  * O^T += V^T P^T: step s covers keys 8(s/4) + 4h + s%4 for lane half h,
+//    the keys of result register s of the score block, so the B operand of
+//    step s is the lane's own probability register s (no exchange, no
+//    rounding). V^T comes from the row-major V tile one float per lane.
+//  * LDS tiles (per wavefront): K rows with their 16-byte chunks XOR-permuted
+//    by the row (the 16 rows read at one chunk position hit distinct banks);
+//    V rows with their 32-float blocks swapped on every other group of four
+//    rows, so the two lane halves of a V^T read (rows four apart) use
+//    disjoint bank halves.
+__device__ __forceinline__ f32x16 mma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads32) void fwd_f32_kernel(FwdParams p) {
-  constexpr int DQ = D / 4;              // d values per lane (4 lanes per query row)
-  constexpr int TILE4 = kBN32 * D / 4;   // float4 per K (or V) tile
-  constexpr int RED = DQ + 2;            // floats per thread in the merge: m, l, O
-  static_assert(kThreads32 * RED <= kSplit32 * 2 * TILE4 * 4, "merge fits in the tile buffers");
-  __shared__ float4 kv_lds[kSplit32][2][TILE4];  // per split: K tile, V tile
+__global__ __launch_bounds__(64 * waves32<D>()) void fwd_f32_kernel(FwdParams p) {
+  constexpr int W = waves32<D>();
+  constexpr int CH = D / 4;     // 16-byte chunks per row
+  constexpr int KU = D / 8;     // K reads per tile (four MFMA steps each)
+  constexpr int DB = D / 32;    // 32-row blocks of O^T
+  constexpr int TILE4 = kBN32 * CH;  // float4 per tile
+  constexpr int RED = 16 * DB + 2;   // floats per lane in the merge: m, l, O
+  static_assert(64 * W * RED <= W * 2 * TILE4 * 4, "merge fits in the tile buffers");
+  __shared__ float4 tiles[W][2][TILE4];  // per wavefront: K tile, V tile
 
   const Work w = map_block(p.n_qtiles, p.Hq, p.group);
   int q0, Lq, k0, Lk;
@@ -592,141 +615,157 @@ __global__ __launch_bounds__(kThreads32) void fwd_f32_kernel(FwdParams p) {
   if (row0 >= Lq) return;
   const int g = w.h / p.group;
   const int tid = threadIdx.x;
-  const int split = __builtin_amdgcn_readfirstlane(tid >> 7);  // two whole waves per split
-  const int t = tid & 127;
-  const int quad = t & 3;
-  const int my_row = row0 + (t >> 2);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int my_row = row0 + l32;
   const int delta = Lk - Lq;
 
   int kv_end = Lk;
   if (CAUSAL) kv_end = min(Lk, row0 + kBM32 + delta);
   const int n_kv = kv_end > 0 ? (kv_end + kBN32 - 1) / kBN32 : 0;
 
-  float q[DQ], o[DQ];
+  // Q fragment: qf[u] = Q[my_row][8u + 4hh .. +3]
+  float4 qf[KU];
   if (my_row < Lq) {
-    const float* src = (const float*)p.q + (int64_t)(q0 + my_row) * p.q_row + (int64_t)w.h * D + quad * DQ;
+    const float* src = (const float*)p.q + (int64_t)(q0 + my_row) * p.q_row + (int64_t)w.h * D + 4 * hh;
 #pragma unroll
-    for (int i = 0; i < DQ; i += 4) {
-      const float4 x = *(const float4*)(src + i);
-      q[i] = x.x; q[i + 1] = x.y; q[i + 2] = x.z; q[i + 3] = x.w;
-    }
+    for (int u = 0; u < KU; ++u) qf[u] = *(const float4*)(src + 8 * u);
   } else {
 #pragma unroll
-    for (int i = 0; i < DQ; ++i) q[i] = 0.f;
+    for (int u = 0; u < KU; ++u) qf[u] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  f32x16 acc_o[DB];
 #pragma unroll
-  for (int i = 0; i < DQ; ++i) o[i] = 0.f;
-  float m_run = neg_inf(), l_run = 0.f;  // log2 domain
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
+  float m_run = neg_inf(), l_run = 0.f;  // log2 domain; l_run: this lane's keys
   const float c2 = p.scale_log2;
   const float* kbase = (const float*)p.k + (int64_t)k0 * p.kv_row + (int64_t)g * D;
   const float* vbase = (const float*)p.v + (int64_t)k0 * p.kv_row + (int64_t)g * D;
-  const float4* k_lds = kv_lds[split][0];
-  const float4* v_lds = kv_lds[split][1];
+  float4* kt = tiles[wave][0];
+  float4* vt = tiles[wave][1];
+  const float* vtf = (const float*)vt;
 
-  const int n_iter = (n_kv + kSplit32 - 1) / kSplit32;
+  const int n_iter = (n_kv + W - 1) / W;
   for (int it = 0; it < n_iter; ++it) {
-    const int j = it * kSplit32 + split;  // this split's tile
-    const bool have = j < n_kv;           // uniform over the split
+    const int j = it * W + wave;  // this wavefront's tile
+    const bool have = j < n_kv;          // uniform over the wavefront
     __syncthreads();
     if (have) {
-      for (int u = t; u < TILE4; u += 128) {
-        const int r = u / (D / 4), c = u % (D / 4);
+      // rows past the sequence end load as zeros (their V must stay finite)
+#pragma unroll
+      for (int n = 0; n < TILE4 / 64; ++n) {
+        const int u = n * 64 + lane;
+        const int r = u / CH, c = u % CH;
         const int key = j * kBN32 + r;
         float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
         if (key < Lk) {
           kv = *(const float4*)(kbase + (int64_t)key * p.kv_row + 4 * c);
           vv = *(const float4*)(vbase + (int64_t)key * p.kv_row + 4 * c);
         }
-        kv_lds[split][0][u] = kv;
-        kv_lds[split][1][u] = vv;
+        kt[r * CH + (c ^ (r & 15))] = kv;
+        vt[r * CH + (c ^ (8 * ((r >> 2) & 1)))] = vv;
       }
     }
     __syncthreads();
     if (!have) continue;
 
-    float s[kBN32];
+    // ---- S^T = K Q^T ----
+    f32x16 sc;
 #pragma unroll
-    for (int jj = 0; jj < kBN32; ++jj) {
-      float part = 0.f;
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
-      for (int i = 0; i < DQ; i += 4) {
-        const float4 kk = k_lds[jj * (D / 4) + quad * (DQ / 4) + i / 4];
-        part = fmaf(q[i], kk.x, part);
-        part = fmaf(q[i + 1], kk.y, part);
-        part = fmaf(q[i + 2], kk.z, part);
-        part = fmaf(q[i + 3], kk.w, part);
-      }
-      part += xor_lane(part, 1);
-      part += xor_lane(part, 2);
-      const int key = j * kBN32 + jj;
-      bool vis = key < Lk;
-      if (CAUSAL) vis = vis && key <= my_row + delta;
-      s[jj] = vis ? part : neg_inf();
+    for (int u = 0; u < KU; ++u) {
+      const float4 kf = kt[l32 * CH + ((2 * u + hh) ^ (l32 & 15))];
+      sc = mma_f32(kf.x, qf[u].x, sc);
+      sc = mma_f32(kf.y, qf[u].y, sc);
+      sc = mma_f32(kf.z, qf[u].z, sc);
+      sc = mma_f32(kf.w, qf[u].w, sc);
     }
+    // ---- mask, online softmax (exact running max) ----
+    // register r holds key j*32 + 8(r/4) + 4hh + r%4
+    const int lim = CAUSAL ? min(Lk - 1, my_row + delta) : Lk - 1;
+    const int thr = lim - j * kBN32 - 4 * hh;
     float mx = neg_inf();
 #pragma unroll
-    for (int jj = 0; jj < kBN32; ++jj) mx = fmaxf(mx, s[jj]);
+    for (int r = 0; r < 16; ++r) {
+      if (8 * (r >> 2) + (r & 3) > thr) sc[r] = neg_inf();
+      mx = fmaxf(mx, sc[r]);
+    }
+    mx = max_halves(mx);
     const float m_new = fmaxf(m_run, mx * c2);
     const float base = (m_new == neg_inf()) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - base);
     float rs = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < kBN32; ++jj) {
-      s[jj] = fast_exp2(fmaf(s[jj], c2, -base));
-      rs += s[jj];
+    for (int r = 0; r < 16; ++r) {
+      sc[r] = fast_exp2(fmaf(sc[r], c2, -base));
+      rs += sc[r];
     }
     l_run = l_run * alpha + rs;
     m_run = m_new;
 #pragma unroll
-    for (int i = 0; i < DQ; ++i) o[i] *= alpha;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int jj = 0; jj < kBN32; ++jj) {
+      for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+    // ---- O^T += V^T P^T ----
 #pragma unroll
-      for (int i = 0; i < DQ; i += 4) {
-        const float4 vv = v_lds[jj * (D / 4) + quad * (DQ / 4) + i / 4];
-        o[i] = fmaf(s[jj], vv.x, o[i]);
-        o[i + 1] = fmaf(s[jj], vv.y, o[i + 1]);
-        o[i + 2] = fmaf(s[jj], vv.z, o[i + 2]);
-        o[i + 3] = fmaf(s[jj], vv.w, o[i + 3]);
-      }
+    for (int st = 0; st < 16; ++st) {
+      const int key = 8 * (st >> 2) + 4 * hh + (st & 3);  // (key >> 2) & 1 == hh
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acc_o[db] = mma_f32(vtf[key * D + 32 * (db ^ hh) + l32], sc[st], acc_o[db]);
     }
   }
 
-  // ---- merge the splits (fixed order), then O = O / l, LSE ----
-  float* red = (float*)&kv_lds[0][0][0];
-  __syncthreads();  // every split is done with its tiles
+  // ---- merge the wavefronts (fixed order), then O = O / l, LSE ----
+  l_run = sum_halves(l_run);
+  float* red = (float*)&tiles[0][0][0];
+  __syncthreads();  // every wavefront is done with its tiles
   {
     float* mine = red + (int64_t)tid * RED;
     mine[0] = m_run;
     mine[1] = l_run;
 #pragma unroll
-    for (int i = 0; i < DQ; ++i) mine[2 + i] = o[i];
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mine[2 + 16 * db + r] = acc_o[db][r];
   }
   __syncthreads();
-  if (split != 0) return;
+  if (wave != 0) return;
   float M = neg_inf();
 #pragma unroll
-  for (int sp = 0; sp < kSplit32; ++sp) M = fmaxf(M, red[(sp * 128 + t) * RED]);
+  for (int wv = 0; wv < W; ++wv) M = fmaxf(M, red[(wv * 64 + lane) * RED]);
   float l_tot = 0.f;
 #pragma unroll
-  for (int i = 0; i < DQ; ++i) o[i] = 0.f;
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
   if (M != neg_inf()) {
 #pragma unroll
-    for (int sp = 0; sp < kSplit32; ++sp) {
-      const float* st = red + (sp * 128 + t) * RED;
+    for (int wv = 0; wv < W; ++wv) {
+      const float* st = red + (wv * 64 + lane) * RED;
       const float ws = st[0] == neg_inf() ? 0.f : fast_exp2(st[0] - M);
       l_tot = fmaf(st[1], ws, l_tot);
 #pragma unroll
-      for (int i = 0; i < DQ; ++i) o[i] = fmaf(st[2 + i], ws, o[i]);
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[db][r] = fmaf(st[2 + 16 * db + r], ws, acc_o[db][r]);
     }
   }
   if (my_row < Lq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* dst = (float*)p.o + (int64_t)(q0 + my_row) * p.q_row + (int64_t)w.h * D + quad * DQ;
+    float* dst = (float*)p.o + (int64_t)(q0 + my_row) * p.q_row + (int64_t)w.h * D;
+    // register r of block db holds d = 32 db + 8(r/4) + 4hh + r%4
 #pragma unroll
-    for (int i = 0; i < DQ; i += 4)
-      *(float4*)(dst + i) = make_float4(o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv);
-    if (quad == 0)
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        *(float4*)(dst + 32 * db + 8 * gq + 4 * hh) =
+            make_float4(acc_o[db][4 * gq] * inv, acc_o[db][4 * gq + 1] * inv,
+                        acc_o[db][4 * gq + 2] * inv, acc_o[db][4 * gq + 3] * inv);
+    if (hh == 0)
       p.lse[(int64_t)(q0 + my_row) * p.Hq + w.h] =
           l_tot > 0.f ? (M + __builtin_log2f(l_tot)) * kLn2 : neg_inf();
   }
@@ -744,9 +783,9 @@ hipError_t launch_mfma(const FwdParams& p, bool causal, int blocks, hipStream_t 
 template <int D>
 hipError_t launch_f32(const FwdParams& p, bool causal, int blocks, hipStream_t st) {
   if (causal)
-    hipLaunchKernelGGL((fwd_f32_kernel<D, true>), dim3(blocks), dim3(kThreads32), 0, st, p);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, true>), dim3(blocks), dim3(64 * waves32<D>()), 0, st, p);
   else
-    hipLaunchKernelGGL((fwd_f32_kernel<D, false>), dim3(blocks), dim3(kThreads32), 0, st, p);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, false>), dim3(blocks), dim3(64 * waves32<D>()), 0, st, p);
   return hipGetLastError();
 }
 
