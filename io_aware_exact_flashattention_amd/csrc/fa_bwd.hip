@@ -68,8 +68,17 @@ template <int D>
 struct Tile {
   static constexpr int ROWB = 2 * D;  // bytes per row
   static constexpr int CH = D / 8;    // 16-byte chunks per row
+  // The permutation serves both read patterns below. Row reads take one
+  // chunk of 16 consecutive rows: swz is one-to-one on those rows. A
+  // transposed read takes two (or, per 32 lanes, four) consecutive chunks of
+  // four consecutive rows: swz / 4 (d = 128) differs between those rows, so
+  // each row's chunks land in a block of four chunk positions of its own.
+  // At d = 64 two rows share 256 bytes; the same holds for the rows of one
+  // parity, with the bits of row / 2 permuted instead.
   __device__ static __forceinline__ int swz(int row) {
-    return CH == 16 ? (row & 15) : ((row >> 1) & 7);
+    if constexpr (CH == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    const int r = (row >> 1) & 7;
+    return ((r & 1) << 2) | (r >> 1);
   }
   __device__ static __forceinline__ int chunk(int row, int c) {
     return row * ROWB + 16 * (c ^ swz(row));
