@@ -33,6 +33,8 @@
 // Causal masks are aligned bottom-right (key j visible to query i iff
 // j <= i + Nk - Nq); tiles that no pair of the workgroup can see are
 // skipped. A row whose saved LSE is -inf (it sees no key) has P = 0.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -130,6 +132,63 @@ struct Stager {
     }
   }
 };
+
+// The MFMAs are written out so that each accumulator keeps one register
+// class: the score blocks S and dP, which the vector ALUs read, in VGPRs;
+// the gradient accumulators, read once at the end, in AGPRs. (Left to
+// itself the compiler placed the scores in AGPRs and moved accumulators
+// between the classes on every tile.) It does not know the latency of an
+// inline-asm MFMA, so the waits for its results are explicit below.
+template <typename T>
+__device__ __forceinline__ void mma_v0(f32x16& d, uint4 a, uint4 b) {  // d = a b
+  const b_u32x4 x = __builtin_bit_cast(b_u32x4, a), y = __builtin_bit_cast(b_u32x4, b);
+  if constexpr (std::is_same<T, Bf16>::value)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(x), "v"(y));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(x), "v"(y));
+}
+template <typename T>
+__device__ __forceinline__ void mma_v(f32x16& d, uint4 a, uint4 b) {  // d += a b
+  const b_u32x4 x = __builtin_bit_cast(b_u32x4, a), y = __builtin_bit_cast(b_u32x4, b);
+  if constexpr (std::is_same<T, Bf16>::value)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(x), "v"(y));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(x), "v"(y));
+}
+template <typename T>
+__device__ __forceinline__ void mma_a(f32x16& d, uint4 a, uint4 b) {  // d += a b, d in AGPRs
+  const b_u32x4 x = __builtin_bit_cast(b_u32x4, a), y = __builtin_bit_cast(b_u32x4, b);
+  if constexpr (std::is_same<T, Bf16>::value)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(x), "v"(y));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(d) : "v"(x), "v"(y));
+}
+// 19 wait states after the MFMAs that wrote S and dP, before anything else
+// touches them (an 8-pass MFMA's result may be read 18 states after issue).
+// S and dP are operands, so no read of them is scheduled ahead of the wait.
+__device__ __forceinline__ void wait_scores(f32x16& a, f32x16& b) {
+  asm volatile("s_nop 15\n\ts_nop 2" : "+v"(a), "+v"(b));
+}
+// 4 wait states between the vector-ALU writes of MFMA B operands and the
+// MFMAs that read them
+__device__ __forceinline__ void wait_operands(uint4 (&a)[2], uint4 (&b)[2]) {
+  b_u32x4 x0 = __builtin_bit_cast(b_u32x4, a[0]), x1 = __builtin_bit_cast(b_u32x4, a[1]);
+  b_u32x4 y0 = __builtin_bit_cast(b_u32x4, b[0]), y1 = __builtin_bit_cast(b_u32x4, b[1]);
+  asm volatile("s_nop 3" : "+v"(x0), "+v"(x1), "+v"(y0), "+v"(y1));
+  a[0] = __builtin_bit_cast(uint4, x0);
+  a[1] = __builtin_bit_cast(uint4, x1);
+  b[0] = __builtin_bit_cast(uint4, y0);
+  b[1] = __builtin_bit_cast(uint4, y1);
+}
+// 19 wait states after the last accumulation, before the epilogue reads the
+// accumulators
+template <int DB>
+__device__ __forceinline__ void wait_acc(f32x16 (&a)[DB]) {
+  if constexpr (DB == 4)
+    asm volatile("s_nop 15\n\ts_nop 2" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
+  else
+    asm volatile("s_nop 15\n\ts_nop 2" : "+a"(a[0]), "+a"(a[1]));
+}
 
 // sum of the products of the eight 16-bit values of a and b, in fp32
 template <typename T>
@@ -252,13 +311,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
       f32x16 st, dp;
+      mma_v0<T>(st, G::row_frag(K, 32 * kb, 0, lane), qf[0]);
+      mma_v0<T>(dp, G::row_frag(V, 32 * kb, 0, lane), df[0]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = dp[r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        st = E::mma32(G::row_frag(K, 32 * kb, s, lane), qf[s], st);
-        dp = E::mma32(G::row_frag(V, 32 * kb, s, lane), df[s], dp);
+      for (int s = 1; s < KS; ++s) {
+        mma_v<T>(st, G::row_frag(K, 32 * kb, s, lane), qf[s]);
+        mma_v<T>(dp, G::row_frag(V, 32 * kb, s, lane), df[s]);
       }
+      wait_scores(st, dp);
       // register r holds key j*64 + 32 kb + 4 hh + 8 (r/4) + r%4 of this row
       const int thr = lim - (j * kDqKeys + 32 * kb + 4 * hh);
       uint4 dsf[2];
@@ -274,13 +334,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdParams p) {
         dsf[u] = make_uint4(E::pack2(e[0], e[1]), E::pack2(e[2], e[3]), E::pack2(e[4], e[5]),
                             E::pack2(e[6], e[7]));
       }
+      wait_operands(dsf, dsf);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          acc[db] = E::mma32(G::tr_frag(K, 32 * kb + 16 * u, db, lane), dsf[u], acc[db]);
+        for (int u = 0; u < 2; ++u) mma_a<T>(acc[db], G::tr_frag(K, 32 * kb + 16 * u, db, lane), dsf[u]);
     }
   }
+  wait_acc<DB>(acc);
   if (row_ok) store_row<T, DB>((uint16_t*)p.dq + qoff, acc, p.scale, hh);
 }
 
@@ -368,13 +429,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x16 st, dp;
+      mma_v0<T>(st, G::row_frag(Q, 32 * qb, 0, lane), kf[0]);
+      mma_v0<T>(dp, G::row_frag(dO, 32 * qb, 0, lane), vf[0]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = dp[r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        st = E::mma32(G::row_frag(Q, 32 * qb, s, lane), kf[s], st);
-        dp = E::mma32(G::row_frag(dO, 32 * qb, s, lane), vf[s], dp);
+      for (int s = 1; s < KS; ++s) {
+        mma_v<T>(st, G::row_frag(Q, 32 * qb, s, lane), kf[s]);
+        mma_v<T>(dp, G::row_frag(dO, 32 * qb, s, lane), vf[s]);
       }
+      wait_scores(st, dp);
       // register r holds query row q0 + 32 qb + 4 hh + 8 (r/4) + r%4 of this key;
       // under the causal mask it is visible iff 8 (r/4) + r%4 >= thr
       const int thr = my_key - delta - (q0 + 32 * qb + 4 * hh);
@@ -402,15 +464,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
         dsf[u] = make_uint4(E::pack2(de[0], de[1]), E::pack2(de[2], de[3]),
                             E::pack2(de[4], de[5]), E::pack2(de[6], de[7]));
       }
+      wait_operands(pf, dsf);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          acc_v[db] = E::mma32(G::tr_frag(dO, 32 * qb + 16 * u, db, lane), pf[u], acc_v[db]);
-          acc_k[db] = E::mma32(G::tr_frag(Q, 32 * qb + 16 * u, db, lane), dsf[u], acc_k[db]);
+          mma_a<T>(acc_v[db], G::tr_frag(dO, 32 * qb + 16 * u, db, lane), pf[u]);
+          mma_a<T>(acc_k[db], G::tr_frag(Q, 32 * qb + 16 * u, db, lane), dsf[u]);
         }
     }
   }
+  wait_acc<DB>(acc_v);
+  wait_acc<DB>(acc_k);
   if (key_ok) {
     store_row<T, DB>((uint16_t*)p.dk + koff, acc_k, p.scale, hh);
     store_row<T, DB>((uint16_t*)p.dv + koff, acc_v, 1.f, hh);
