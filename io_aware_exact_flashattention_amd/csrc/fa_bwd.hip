@@ -106,32 +106,32 @@ struct Tile {
   }
 };
 
-// Registers that stage a ROWS x D tile on its way from device memory to
-// LDS: rows at or past `valid` are zero.
+// Direct-to-LDS copy of a ROWS x D tile (global_load_lds_dwordx4, no
+// registers held while in flight). Load n of thread tid fills LDS chunk
+// n * 256 + tid of the tile, so each wavefront instruction writes 1 KB
+// contiguously; the lane fetches the logical chunk that Tile<D>'s
+// permutation puts there. Rows at or past `valid` repeat row valid - 1:
+// the callers give their products a zero weight (masked keys; query rows
+// with P = 0).
 template <int D, int ROWS>
-struct Stager {
+struct TileCopy {
   static constexpr int CH = D / 8;
-  static constexpr int N = ROWS * CH / kBwdThreads;  // 16-byte pieces per thread
+  static constexpr int N = ROWS * CH / kBwdThreads;  // loads per thread
   static_assert(N * kBwdThreads == ROWS * CH, "tile pieces");
-  uint4 r[N];
-  __device__ __forceinline__ void load(const uint16_t* base, int64_t stride, int row0, int valid,
-                                       int tid) {
+  __device__ static __forceinline__ void issue(const uint16_t* base, int64_t stride, int row0,
+                                               int valid, uint32_t lds_tile, int wave, int lane) {
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      const int idx = n * kBwdThreads + tid, row = idx / CH, c = idx % CH;
-      r[n] = row0 + row < valid
-                 ? *(const uint4*)(base + (int64_t)(row0 + row) * stride + 8 * c)
-                 : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(char* t, int tid) const {
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-      const int idx = n * kBwdThreads + tid, row = idx / CH, c = idx % CH;
-      *(uint4*)(t + Tile<D>::chunk(row, c)) = r[n];
+      const int idx = n * kBwdThreads + wave * 64 + lane, row = idx / CH;
+      const int c = (idx % CH) ^ Tile<D>::swz(row);
+      const int r = min(row0 + row, valid - 1);
+      load_to_lds(base + (int64_t)r * stride + 8 * c, lds_tile + 16 * (n * kBwdThreads + wave * 64));
     }
   }
 };
+__device__ __forceinline__ void wait_tile_copies() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 // The MFMAs are written out so that each accumulator keeps one register
 // class: the score blocks S and dP, which the vector ALUs read, in VGPRs;
@@ -289,23 +289,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdParams p) {
 
   const uint16_t* kbase = (const uint16_t*)p.k + (int64_t)b * Lk * p.kv_row + (int64_t)g * D;
   const uint16_t* vbase = (const uint16_t*)p.v + (int64_t)b * Lk * p.kv_row + (int64_t)g * D;
-  Stager<D, kDqKeys> sk, sv;
-  if (n_kv > 0) {
-    sk.load(kbase, p.kv_row, 0, Lk, tid);
-    sv.load(vbase, p.kv_row, 0, Lk, tid);
-  }
+  const uint32_t lds0 = lds_address(lds);
+  using Copy = TileCopy<D, kDqKeys>;
+  auto issue = [&](int j) {
+    const uint32_t t0 = lds0 + (j & 1) * 2 * TB;
+    Copy::issue(kbase, p.kv_row, j * kDqKeys, Lk, t0, wave, lane);
+    Copy::issue(vbase, p.kv_row, j * kDqKeys, Lk, t0 + TB, wave, lane);
+  };
+  if (n_kv > 0) issue(0);
   for (int j = 0; j < n_kv; ++j) {
     char* kt = lds[j & 1][0];
     char* vt = lds[j & 1][1];
-    // the buffer written here was last read in iteration j - 2, before
-    // every thread passed the barrier of iteration j - 1
-    sk.store(kt, tid);
-    sv.store(vt, tid);
+    // tile j complete everywhere; tile j + 1 goes to the other buffer, last
+    // read in iteration j - 1, before every thread passed this barrier
+    wait_tile_copies();
     __syncthreads();
-    if (j + 1 < n_kv) {
-      sk.load(kbase, p.kv_row, (j + 1) * kDqKeys, Lk, tid);
-      sv.load(vbase, p.kv_row, (j + 1) * kDqKeys, Lk, tid);
-    }
+    if (j + 1 < n_kv) issue(j + 1);
     b_lds_cchar* K = (b_lds_cchar*)kt;
     b_lds_cchar* V = (b_lds_cchar*)vt;
 #pragma unroll
@@ -400,14 +399,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_k[db][r] = acc_v[db][r] = 0.f;
 
-  Stager<D, kKvRows> sq, sd;
+  const uint32_t lds0 = lds_address(lds);
+  using Copy = TileCopy<D, kKvRows>;
   float sr = 0.f;  // thread tid < 2*kKvRows stages one lse offset or D value
   auto load = [&](int it) {
     const int h = g * p.group + it / n_qt;
     const int q0 = (qt0 + it % n_qt) * kKvRows;
     const int64_t base = (int64_t)b * Lq * p.q_row + (int64_t)h * D;
-    sq.load((const uint16_t*)p.q + base, p.q_row, q0, Lq, tid);
-    sd.load((const uint16_t*)p.dout + base, p.q_row, q0, Lq, tid);
+    const uint32_t t0 = lds0 + (it & 1) * 2 * TB;
+    Copy::issue((const uint16_t*)p.q + base, p.q_row, q0, Lq, t0, wave, lane);
+    Copy::issue((const uint16_t*)p.dout + base, p.q_row, q0, Lq, t0 + TB, wave, lane);
     if (tid < 2 * kKvRows) {
       const int row = q0 + (tid % kKvRows);
       const int64_t li = ((int64_t)b * Lq + row) * p.Hq + h;
@@ -418,9 +419,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
   if (n_it > 0) load(0);
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
-    sq.store(lds[buf][0], tid);
-    sd.store(lds[buf][1], tid);
+    // Q/dO tile it complete everywhere; tile it + 1 goes to the other
+    // buffer, last read in iteration it - 1, before every thread passed
+    // this barrier
     if (tid < 2 * kKvRows) lds_r[buf][tid / kKvRows][tid % kKvRows] = sr;
+    wait_tile_copies();
     __syncthreads();
     const int q0 = (qt0 + it % n_qt) * kKvRows;
     if (it + 1 < n_it) load(it + 1);
