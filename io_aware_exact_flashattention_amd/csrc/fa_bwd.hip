@@ -46,6 +46,22 @@ constexpr int kDqRows = 128;      // query rows per workgroup of the dQ kernel
 constexpr int kDqKeys = 64;       // keys per K/V tile of the dQ kernel
 constexpr int kKvKeys = 128;      // keys per workgroup of the dK/dV kernel
 constexpr int kKvRows = 64;       // query rows per Q/dO tile of the dK/dV kernel
+constexpr int kRing = 3;          // LDS buffers of the Q/dO tile ring
+
+// Calls f(std::integral_constant<int, i>) for i = I .. N-1: the index is a
+// constant expression in the body.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+// Keep a value's computation ahead of this point (an empty volatile asm
+// uses it; the compiler does not move volatile asm across the scheduling
+// fences that lay out the MFMA/softmax interleave).
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
 typedef short b_s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) b_s16x4 b_lds_s16x4;
@@ -179,6 +195,16 @@ __device__ __forceinline__ void wait_operands(uint4 (&a)[2], uint4 (&b)[2]) {
   a[1] = __builtin_bit_cast(uint4, x1);
   b[0] = __builtin_bit_cast(uint4, y0);
   b[1] = __builtin_bit_cast(uint4, y1);
+}
+// the same for two accumulator sets
+template <int DB>
+__device__ __forceinline__ void wait_acc2(f32x16 (&a)[DB], f32x16 (&b)[DB]) {
+  if constexpr (DB == 4)
+    asm volatile("s_nop 15\n\ts_nop 2"
+                 : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(b[0]), "+a"(b[1]),
+                   "+a"(b[2]), "+a"(b[3]));
+  else
+    asm volatile("s_nop 15\n\ts_nop 2" : "+a"(a[0]), "+a"(a[1]), "+a"(b[0]), "+a"(b[1]));
 }
 // 19 wait states after the last accumulation, before the epilogue reads the
 // accumulators
@@ -352,8 +378,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int DB = D / 32;
   constexpr int QB = kKvRows / 32;  // 32-row blocks per Q/dO tile
   constexpr int TB = kKvRows * G::ROWB;
-  __shared__ __attribute__((aligned(16))) char lds[2][2][TB];  // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float lds_r[2][2][kKvRows];  // [buffer][offset, D]
+  constexpr int RING = D == 128 ? kRing : 2;
+  __shared__ __attribute__((aligned(16))) char lds[RING][2][TB];  // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float lds_r[RING][2][kKvRows];  // [buffer][offset, D]
 
   // work item (sequence b, key/value head g, key tile t); under a causal
   // mask the first key tiles see the most queries and come first
@@ -399,6 +426,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_k[db][r] = acc_v[db][r] = 0.f;
 
+  // Q/dO tiles go through a ring of RING LDS buffers: the barrier opening
+  // tile it issues the copies of tile it + 1 into the buffer of tile
+  // it + 1 - RING, whose last reads every wave has finished by then (with
+  // the pipeline below, the gradients of tile it - 1 still read their
+  // buffer after that barrier, hence three buffers at d = 128).
   const uint32_t lds0 = lds_address(lds);
   using Copy = TileCopy<D, kKvRows>;
   float sr = 0.f;  // thread tid < 2*kKvRows stages one lse offset or D value
@@ -406,7 +438,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
     const int h = g * p.group + it / n_qt;
     const int q0 = (qt0 + it % n_qt) * kKvRows;
     const int64_t base = (int64_t)b * Lq * p.q_row + (int64_t)h * D;
-    const uint32_t t0 = lds0 + (it & 1) * 2 * TB;
+    const uint32_t t0 = lds0 + (it % RING) * 2 * TB;
     Copy::issue((const uint16_t*)p.q + base, p.q_row, q0, Lq, t0, wave, lane);
     Copy::issue((const uint16_t*)p.dout + base, p.q_row, q0, Lq, t0 + TB, wave, lane);
     if (tid < 2 * kKvRows) {
@@ -416,65 +448,192 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
       else sr = row < Lq ? p.dsum[li] : 0.f;
     }
   };
-  if (n_it > 0) load(0);
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
-    // Q/dO tile it complete everywhere; tile it + 1 goes to the other
-    // buffer, last read in iteration it - 1, before every thread passed
-    // this barrier
-    if (tid < 2 * kKvRows) lds_r[buf][tid / kKvRows][tid % kKvRows] = sr;
+  auto open_tile = [&](int it) {
+    if (tid < 2 * kKvRows) lds_r[it % RING][tid / kKvRows][tid % kKvRows] = sr;
     wait_tile_copies();
     __syncthreads();
-    const int q0 = (qt0 + it % n_qt) * kKvRows;
     if (it + 1 < n_it) load(it + 1);
-    b_lds_cchar* Q = (b_lds_cchar*)lds[buf][0];
-    b_lds_cchar* dO = (b_lds_cchar*)lds[buf][1];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x16 st, dp;
-      mma_v0<T>(st, G::row_frag(Q, 32 * qb, 0, lane), kf[0]);
-      mma_v0<T>(dp, G::row_frag(dO, 32 * qb, 0, lane), vf[0]);
-#pragma unroll
-      for (int s = 1; s < KS; ++s) {
-        mma_v<T>(st, G::row_frag(Q, 32 * qb, s, lane), kf[s]);
-        mma_v<T>(dp, G::row_frag(dO, 32 * qb, s, lane), vf[s]);
+  };
+  auto qtile = [&](int it) { return (b_lds_cchar*)lds[it % RING][0]; };
+  auto dotile = [&](int it) { return (b_lds_cchar*)lds[it % RING][1]; };
+
+  // The 32-row blocks m = QB it + qb run as a pipeline in one wave: slot m
+  // issues the 16 score MFMAs of block m + 1 (S = Q K^T, dP = dO V^T; lane
+  // = key), each followed by one element of block m's softmax (P and
+  // dS = P o (dP - D) for one query row), then the 16 gradient MFMAs of
+  // block m (dV^T += dO^T P, dK^T += Q^T dS). The matrix core then has the
+  // next block's MFMAs to run while the vector ALUs work on the current
+  // block. Scores alternate between two register sets by block parity.
+  f32x16 sA, dA, sB, dB;
+  // scores of block (it, qb) into (sn, dn), each MFMA followed by element
+  // j of the softmax of the block (itc, qbc) in (sc, dc) when soft is set
+  auto slot = [&](int it, int qb, f32x16& sc, f32x16& dc, f32x16& sn, f32x16& dn, int itn,
+                  int qbn, auto next_c, auto soft_c) {
+    constexpr bool has_next = decltype(next_c)::value;
+    constexpr bool soft = decltype(soft_c)::value;
+    b_lds_cchar* Qn = qtile(itn);
+    b_lds_cchar* dOn = dotile(itn);
+    const int buf = it % RING;
+    const int q0 = (qt0 + it % n_qt) * kKvRows;
+    // register r holds query row q0 + 32 qb + 4 hh + 8 (r/4) + r%4 of this
+    // key; under the causal mask it is visible iff 8 (r/4) + r%4 >= thr
+    const int thr = my_key - delta - (q0 + 32 * qb + 4 * hh);
+    float pe0 = 0.f, de0 = 0.f, ov[4], dv[4];
+    uint32_t pw[8], dw[8];  // P and dS of the block, packed to 16 bits
+    uint4 fr[2];
+    if constexpr (has_next) fr[0] = G::row_frag(Qn, 32 * qbn, 0, lane);
+    // 16 steps, one softmax element each; the 2 KS score MFMAs go to every
+    // STEP-th step (MFMA mi: k-step mi / 2, S for even mi, dP for odd)
+    constexpr int STEP = 16 / (2 * KS);
+    static_assert(STEP * 2 * KS == 16, "score MFMAs per block");
+    static_for<0, 16>([&](auto j_c) {
+      constexpr int j = decltype(j_c)::value;
+      if constexpr (has_next && j % STEP == 0) {
+        constexpr int mi = j / STEP, s = mi / 2;
+        if constexpr (mi + 1 < 2 * KS)
+          fr[(mi + 1) & 1] = G::row_frag(((mi + 1) & 1) ? dOn : Qn, 32 * qbn, (mi + 1) / 2, lane);
+        if constexpr (mi & 1) {
+          if constexpr (s == 0) mma_v0<T>(dn, fr[1], vf[0]);
+          else mma_v<T>(dn, fr[1], vf[s]);
+        } else {
+          if constexpr (s == 0) mma_v0<T>(sn, fr[0], kf[0]);
+          else mma_v<T>(sn, fr[0], kf[s]);
+        }
       }
-      wait_scores(st, dp);
-      // register r holds query row q0 + 32 qb + 4 hh + 8 (r/4) + r%4 of this key;
-      // under the causal mask it is visible iff 8 (r/4) + r%4 >= thr
-      const int thr = my_key - delta - (q0 + 32 * qb + 4 * hh);
-      uint4 pf[2], dsf[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float pe[8], de[8];
-#pragma unroll
-        for (int gq = 0; gq < 2; ++gq) {
-          const int rb = 32 * qb + 8 * (2 * u + gq) + 4 * hh;  // first of four rows
+      if constexpr (soft) {
+        constexpr int r = j, gq = r / 4, i = r % 4;
+        if constexpr (i == 0) {
+          const int rb = 32 * qb + 8 * gq + 4 * hh;  // first of four rows
           const float4 o4 = *(const float4*)&lds_r[buf][0][rb];
           const float4 d4 = *(const float4*)&lds_r[buf][1][rb];
-          const float ov[4] = {o4.x, o4.y, o4.z, o4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 8 * u + 4 * gq + i;
-            const bool vis = !CAUSAL || (8 * (r >> 2) + (r & 3) >= thr);
-            const float pv = vis ? fast_exp2(fmaf(st[r], c2, -ov[i])) : 0.f;
-            pe[4 * gq + i] = pv;
-            de[4 * gq + i] = pv * (dp[r] - dv[i]);
-          }
+          ov[0] = o4.x; ov[1] = o4.y; ov[2] = o4.z; ov[3] = o4.w;
+          dv[0] = d4.x; dv[1] = d4.y; dv[2] = d4.z; dv[3] = d4.w;
         }
-        pf[u] = make_uint4(E::pack2(pe[0], pe[1]), E::pack2(pe[2], pe[3]), E::pack2(pe[4], pe[5]),
-                           E::pack2(pe[6], pe[7]));
-        dsf[u] = make_uint4(E::pack2(de[0], de[1]), E::pack2(de[2], de[3]),
-                            E::pack2(de[4], de[5]), E::pack2(de[6], de[7]));
+        const bool vis = !CAUSAL || (8 * gq + i >= thr);
+        float e = fast_exp2(fmaf(sc[r], c2, -ov[i]));
+        pin(e);  // computed for every lane, then selected: no branch
+        const float pv = vis ? e : 0.f;
+        const float dsv = pv * (dc[r] - dv[i]);
+        if constexpr (r % 2 == 0) {
+          pe0 = pv;
+          de0 = dsv;
+        } else {  // registers r - 1, r: one 32-bit word of each operand
+          pw[r / 2] = E::pack2(pe0, pv);
+          dw[r / 2] = E::pack2(de0, dsv);
+          pin(pw[r / 2]);
+          pin(dw[r / 2]);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (has_next) wait_scores(sn, dn);
+    if constexpr (soft) {
+      uint4 pf[2] = {make_uint4(pw[0], pw[1], pw[2], pw[3]), make_uint4(pw[4], pw[5], pw[6], pw[7])};
+      uint4 dsf[2] = {make_uint4(dw[0], dw[1], dw[2], dw[3]), make_uint4(dw[4], dw[5], dw[6], dw[7])};
       wait_operands(pf, dsf);
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          mma_a<T>(acc_v[db], G::tr_frag(dO, 32 * qb + 16 * u, db, lane), pf[u]);
-          mma_a<T>(acc_k[db], G::tr_frag(Q, 32 * qb + 16 * u, db, lane), dsf[u]);
+      b_lds_cchar* Q = qtile(it);
+      b_lds_cchar* dO = dotile(it);
+      uint4 ta[2], tb[2];
+      ta[0] = G::tr_frag(dO, 32 * qb, 0, lane);
+      tb[0] = G::tr_frag(Q, 32 * qb, 0, lane);
+      static_for<0, 2 * DB>([&](auto k_c) {
+        constexpr int k = decltype(k_c)::value, db = k / 2, u = k % 2;
+        if constexpr (k + 1 < 2 * DB) {
+          ta[(k + 1) & 1] = G::tr_frag(dO, 32 * qb + 16 * ((k + 1) % 2), (k + 1) / 2, lane);
+          tb[(k + 1) & 1] = G::tr_frag(Q, 32 * qb + 16 * ((k + 1) % 2), (k + 1) / 2, lane);
         }
+        mma_a<T>(acc_v[db], ta[k & 1], pf[u]);
+        mma_a<T>(acc_k[db], tb[k & 1], dsf[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // every accumulation complete before the compiler may move an
+      // accumulator for its own register allocation
+      wait_acc2<DB>(acc_v, acc_k);
+    }
+  };
+
+  std::integral_constant<bool, true> yes;
+  std::integral_constant<bool, false> no;
+  static_assert(QB == 2, "two blocks per tile");
+  if constexpr (D == 128) {
+    if (n_it > 0) {
+      load(0);
+      open_tile(0);
+      slot(0, 0, sA, dA, sA, dA, 0, 0, yes, no);  // scores of block 0 only
+      for (int it = 0; it + 1 < n_it; ++it) {
+        // block (it, 0): the scores of (it, 1) come from the same tile
+        slot(it, 0, sA, dA, sB, dB, it, 1, yes, yes);
+        // block (it, 1): the scores of (it + 1, 0) need tile it + 1 opened
+        open_tile(it + 1);
+        slot(it, 1, sB, dB, sA, dA, it + 1, 0, yes, yes);
+      }
+      const int il = n_it - 1;
+      slot(il, 0, sA, dA, sB, dB, il, 1, yes, yes);
+      slot(il, 1, sB, dB, sA, dA, il, 0, no, yes);
+    }
+  } else {
+    // d = 64: the blocks one after the other (the pipeline's second score set
+    // would cost the second workgroup per CU that this variant otherwise has)
+    if (n_it > 0) load(0);
+    for (int it = 0; it < n_it; ++it) {
+      const int buf = it % RING;
+      // Q/dO tile it complete everywhere; tile it + 1 goes to the other
+      // buffer, last read in iteration it - 1, before every thread passed
+      // this barrier
+      if (tid < 2 * kKvRows) lds_r[buf][tid / kKvRows][tid % kKvRows] = sr;
+      wait_tile_copies();
+      __syncthreads();
+      const int q0 = (qt0 + it % n_qt) * kKvRows;
+      if (it + 1 < n_it) load(it + 1);
+      b_lds_cchar* Q = (b_lds_cchar*)lds[buf][0];
+      b_lds_cchar* dO = (b_lds_cchar*)lds[buf][1];
+  #pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x16 st, dp;
+        mma_v0<T>(st, G::row_frag(Q, 32 * qb, 0, lane), kf[0]);
+        mma_v0<T>(dp, G::row_frag(dO, 32 * qb, 0, lane), vf[0]);
+  #pragma unroll
+        for (int s = 1; s < KS; ++s) {
+          mma_v<T>(st, G::row_frag(Q, 32 * qb, s, lane), kf[s]);
+          mma_v<T>(dp, G::row_frag(dO, 32 * qb, s, lane), vf[s]);
+        }
+        wait_scores(st, dp);
+        // register r holds query row q0 + 32 qb + 4 hh + 8 (r/4) + r%4 of this key;
+        // under the causal mask it is visible iff 8 (r/4) + r%4 >= thr
+        const int thr = my_key - delta - (q0 + 32 * qb + 4 * hh);
+        uint4 pf[2], dsf[2];
+  #pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float pe[8], de[8];
+  #pragma unroll
+          for (int gq = 0; gq < 2; ++gq) {
+            const int rb = 32 * qb + 8 * (2 * u + gq) + 4 * hh;  // first of four rows
+            const float4 o4 = *(const float4*)&lds_r[buf][0][rb];
+            const float4 d4 = *(const float4*)&lds_r[buf][1][rb];
+            const float ov[4] = {o4.x, o4.y, o4.z, o4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 8 * u + 4 * gq + i;
+              const bool vis = !CAUSAL || (8 * (r >> 2) + (r & 3) >= thr);
+              const float pv = vis ? fast_exp2(fmaf(st[r], c2, -ov[i])) : 0.f;
+              pe[4 * gq + i] = pv;
+              de[4 * gq + i] = pv * (dp[r] - dv[i]);
+            }
+          }
+          pf[u] = make_uint4(E::pack2(pe[0], pe[1]), E::pack2(pe[2], pe[3]), E::pack2(pe[4], pe[5]),
+                             E::pack2(pe[6], pe[7]));
+          dsf[u] = make_uint4(E::pack2(de[0], de[1]), E::pack2(de[2], de[3]),
+                              E::pack2(de[4], de[5]), E::pack2(de[6], de[7]));
+        }
+        wait_operands(pf, dsf);
+  #pragma unroll
+        for (int db = 0; db < DB; ++db)
+  #pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            mma_a<T>(acc_v[db], G::tr_frag(dO, 32 * qb + 16 * u, db, lane), pf[u]);
+            mma_a<T>(acc_k[db], G::tr_frag(Q, 32 * qb + 16 * u, db, lane), dsf[u]);
+          }
+      }
     }
   }
   wait_acc<DB>(acc_v);
