@@ -24,7 +24,11 @@
 //    the Q/dO tiles (with their lse and D) of every query head of the group
 //    through LDS. Per 32-row block it forms S = Q K^T and dP = dO V^T (a
 //    lane owns one key), P and dS, then dV^T += dO^T P and dK^T += Q^T dS
-//    with dO^T and Q^T read transposed from the tiles.
+//    with dO^T and Q^T read transposed from the tiles. At d = 128 a wave
+//    runs its blocks as a two-stage pipeline: the score MFMAs of the next
+//    block are interleaved with the softmax of the current one.
+// Tiles reach LDS by direct-to-LDS copies; S and dP live in VGPRs and the
+// gradient accumulators in AGPRs (inline-asm MFMAs with explicit waits).
 // The score and probability fragments of one product are the B operands of
 // the next: in a 32x32 MFMA result lane l holds column l % 32 and rows
 // 8(r/4) + 4(l/32) + r%4 of its 16 registers r, so registers 8u .. 8u+7
