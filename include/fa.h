@@ -288,8 +288,10 @@ size_t fa_bwd_workspace_size(int B, int Nq, int Hq);
  *     of every query head that reads it
  *   workspace  at least fa_bwd_workspace_size(B, Nq, Hq) bytes of device
  *     memory owned by the caller (scratch: rowsum(dO o O) per row and head)
- * dtype FA_F16 or FA_BF16; causal masks as for fa_fwd (bottom-right). Two
- * kernels on `stream`, deterministic (fixed summation order, no atomics).
+ * B, Nq, Nk, Hq, Hkv >= 1 and a workspace of at least the stated size, else
+ * FA_ERR_INVALID_ARG; dtype FA_F16 or FA_BF16 (FA_F32: FA_ERR_UNSUPPORTED);
+ * causal masks as for fa_fwd (bottom-right). Two kernels on `stream`,
+ * deterministic (fixed summation order, no atomics).
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  const void* dout, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq,
