@@ -522,6 +522,8 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_heads)
+        # the same work rate on the GPU over the oracle's on the host
+        out["cpu_baseline"]["gpu_over_oracle"] = out["value"] / out["cpu_baseline"]["value"]
     print(json.dumps(out), flush=True)
     if not parity_ok:
         log("[bench] the timed outputs do not match the oracle")
