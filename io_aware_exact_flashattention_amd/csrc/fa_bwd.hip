@@ -50,7 +50,7 @@ constexpr int kDqRows = 128;      // query rows per workgroup of the dQ kernel
 constexpr int kDqKeys = 64;       // keys per K/V tile of the dQ kernel
 constexpr int kKvKeys = 128;      // keys per workgroup of the dK/dV kernel
 constexpr int kKvRows = 64;       // query rows per Q/dO tile of the dK/dV kernel
-constexpr int kRing = 3;          // LDS buffers of the Q/dO tile ring
+constexpr int kRing = 3;          // LDS buffers of the dK/dV kernel's Q/dO tile ring (d = 128)
 
 // Calls f(std::integral_constant<int, i>) for i = I .. N-1: the index is a
 // constant expression in the body.
