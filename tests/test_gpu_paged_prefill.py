@@ -102,3 +102,17 @@ def test_page_permutation_and_poison_bitwise():
     assert torch.equal(oa, ob) and torch.equal(la, lb)
     assert torch.equal(ob, oc) and torch.equal(lb, lc)
     assert not torch.isnan(oc).any()
+
+
+def test_paged_prefill_at_the_page_table_limit():
+    """A sequence of 8192 pages (131072 keys), the most one page-table row
+    staged in LDS may hold, beside a short one; the chunk is the last 64
+    tokens. max_pages = 8193 is refused before any launch."""
+    x = fi.paged_prefill([64, 300], [131072, 300], 2, 1, 128, "bf16", seed=64)
+    assert x.kv.page_table.shape[1] == 8192
+    check(x, "paged prefill at 8192 pages per sequence")
+    q, kp, vp, cq, pt, sl = dev_inputs(x)
+    wide = torch.full((2, 8193), -1, dtype=torch.int32, device="cuda")
+    wide[:, :8192] = pt
+    with pytest.raises(RuntimeError):
+        fa.fwd_paged(q, kp, vp, cq, wide, sl, x.max_q, causal=True, scale=x.kv.scale)

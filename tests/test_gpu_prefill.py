@@ -177,3 +177,20 @@ def test_causal_more_queries_than_keys_empty_rows():
     O, L = oracle.attention(fi.to_f64(x.q, "bf16"), fi.to_f64(x.k, "bf16"), fi.to_f64(x.v, "bf16"),
                             x.scale, True)
     assert_parity(o, l, O, L, fi.to_f64(x.v, "bf16"), "bf16", "Nq>Nk causal")
+
+
+def test_long_single_head_sampled_rows():
+    """One causal head of 65536 tokens (256 query tiles, 512 key tiles):
+    rows at both ends, at tile boundaries and in between against the oracle
+    over all their keys."""
+    x = fi.dense(1, 65536, 65536, 1, 1, 128, "bf16", seed=65, causal=True)
+    q, k, v = dense_dev(x)
+    o, l = fa.fwd(q, k, v, causal=True, scale=x.scale)
+    torch.cuda.synchronize()
+    o, l = to_f64(o), to_f64(l)
+    rows = np.array([0, 1, 255, 256, 4095, 32767, 32768, 65279, 65280, 65535])
+    O, L = oracle.attention_rows(fi.to_f64(x.q[0, rows, 0], "bf16"), rows, 65536,
+                                 fi.to_f64(x.k[0, :, 0], "bf16"), fi.to_f64(x.v[0, :, 0], "bf16"),
+                                 x.scale, True)
+    assert_parity(o[0, rows, 0], l[0, rows, 0], O, L, fi.to_f64(x.v[0, :, 0], "bf16"), "bf16",
+                  "long head N=65536 sampled rows")
