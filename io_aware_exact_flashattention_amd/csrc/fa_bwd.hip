@@ -482,42 +482,57 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
     // register r holds query row q0 + 32 qb + 4 hh + 8 (r/4) + r%4 of this
     // key; under the causal mask it is visible iff 8 (r/4) + r%4 >= thr
     const int thr = my_key - delta - (q0 + 32 * qb + 4 * hh);
-    float pe0 = 0.f, de0 = 0.f, ov[4], dv[4];
+    float pe0 = 0.f, de0 = 0.f;
     uint32_t pw[8], dw[8];  // P and dS of the block, packed to 16 bits
-    uint4 fr[2];
-    if constexpr (has_next) fr[0] = G::row_frag(Qn, 32 * qbn, 0, lane);
+    // the block's lse offsets and D values, read before its 16 steps so that
+    // their LDS latency is not waited out inside them
+    float ov[16], dv[16];
+    if constexpr (soft) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int rb = 32 * qb + 8 * gq + 4 * hh;  // first of four rows
+        const float4 o4 = *(const float4*)&lds_r[buf][0][rb];
+        const float4 d4 = *(const float4*)&lds_r[buf][1][rb];
+        ov[4 * gq] = o4.x; ov[4 * gq + 1] = o4.y; ov[4 * gq + 2] = o4.z; ov[4 * gq + 3] = o4.w;
+        dv[4 * gq] = d4.x; dv[4 * gq + 1] = d4.y; dv[4 * gq + 2] = d4.z; dv[4 * gq + 3] = d4.w;
+      }
+    }
+    // score fragments read AHEAD MFMAs ahead of their use, in a ring of
+    // AHEAD + 1 register sets (one MFMA plus one softmax element covers
+    // only a fraction of an LDS read's latency)
+    constexpr int AHEAD = 3;
+    uint4 fr[AHEAD + 1];
     // 16 steps, one softmax element each; the 2 KS score MFMAs go to every
     // STEP-th step (MFMA mi: k-step mi / 2, S for even mi, dP for odd)
     constexpr int STEP = 16 / (2 * KS);
     static_assert(STEP * 2 * KS == 16, "score MFMAs per block");
+    if constexpr (has_next)
+      static_for<0, AHEAD>([&](auto m_c) {
+        constexpr int m = decltype(m_c)::value;
+        if constexpr (m < 2 * KS) fr[m] = G::row_frag((m & 1) ? dOn : Qn, 32 * qbn, m / 2, lane);
+      });
     static_for<0, 16>([&](auto j_c) {
       constexpr int j = decltype(j_c)::value;
       if constexpr (has_next && j % STEP == 0) {
-        constexpr int mi = j / STEP, s = mi / 2;
-        if constexpr (mi + 1 < 2 * KS)
-          fr[(mi + 1) & 1] = G::row_frag(((mi + 1) & 1) ? dOn : Qn, 32 * qbn, (mi + 1) / 2, lane);
+        constexpr int mi = j / STEP, s = mi / 2, nx = mi + AHEAD;
+        if constexpr (nx < 2 * KS)
+          fr[nx % (AHEAD + 1)] = G::row_frag((nx & 1) ? dOn : Qn, 32 * qbn, nx / 2, lane);
+        constexpr int fi = mi % (AHEAD + 1);
         if constexpr (mi & 1) {
-          if constexpr (s == 0) mma_v0<T>(dn, fr[1], vf[0]);
-          else mma_v<T>(dn, fr[1], vf[s]);
+          if constexpr (s == 0) mma_v0<T>(dn, fr[fi], vf[0]);
+          else mma_v<T>(dn, fr[fi], vf[s]);
         } else {
-          if constexpr (s == 0) mma_v0<T>(sn, fr[0], kf[0]);
-          else mma_v<T>(sn, fr[0], kf[s]);
+          if constexpr (s == 0) mma_v0<T>(sn, fr[fi], kf[0]);
+          else mma_v<T>(sn, fr[fi], kf[s]);
         }
       }
       if constexpr (soft) {
         constexpr int r = j, gq = r / 4, i = r % 4;
-        if constexpr (i == 0) {
-          const int rb = 32 * qb + 8 * gq + 4 * hh;  // first of four rows
-          const float4 o4 = *(const float4*)&lds_r[buf][0][rb];
-          const float4 d4 = *(const float4*)&lds_r[buf][1][rb];
-          ov[0] = o4.x; ov[1] = o4.y; ov[2] = o4.z; ov[3] = o4.w;
-          dv[0] = d4.x; dv[1] = d4.y; dv[2] = d4.z; dv[3] = d4.w;
-        }
         const bool vis = !CAUSAL || (8 * gq + i >= thr);
-        float e = fast_exp2(fmaf(sc[r], c2, -ov[i]));
+        float e = fast_exp2(fmaf(sc[r], c2, -ov[r]));
         pin(e);  // computed for every lane, then selected: no branch
         const float pv = vis ? e : 0.f;
-        const float dsv = pv * (dc[r] - dv[i]);
+        const float dsv = pv * (dc[r] - dv[r]);
         if constexpr (r % 2 == 0) {
           pe0 = pv;
           de0 = dsv;
@@ -537,17 +552,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
       wait_operands(pf, dsf);
       b_lds_cchar* Q = qtile(it);
       b_lds_cchar* dO = dotile(it);
-      uint4 ta[2], tb[2];
-      ta[0] = G::tr_frag(dO, 32 * qb, 0, lane);
-      tb[0] = G::tr_frag(Q, 32 * qb, 0, lane);
+      // transposed fragments two MFMA pairs ahead, in a ring of three
+      uint4 ta[3], tb[3];
+      static_for<0, 2>([&](auto m_c) {
+        constexpr int m = decltype(m_c)::value;
+        ta[m] = G::tr_frag(dO, 32 * qb + 16 * (m % 2), m / 2, lane);
+        tb[m] = G::tr_frag(Q, 32 * qb + 16 * (m % 2), m / 2, lane);
+      });
       static_for<0, 2 * DB>([&](auto k_c) {
-        constexpr int k = decltype(k_c)::value, db = k / 2, u = k % 2;
-        if constexpr (k + 1 < 2 * DB) {
-          ta[(k + 1) & 1] = G::tr_frag(dO, 32 * qb + 16 * ((k + 1) % 2), (k + 1) / 2, lane);
-          tb[(k + 1) & 1] = G::tr_frag(Q, 32 * qb + 16 * ((k + 1) % 2), (k + 1) / 2, lane);
+        constexpr int k = decltype(k_c)::value, db = k / 2, u = k % 2, nx = k + 2;
+        if constexpr (nx < 2 * DB) {
+          ta[nx % 3] = G::tr_frag(dO, 32 * qb + 16 * (nx % 2), nx / 2, lane);
+          tb[nx % 3] = G::tr_frag(Q, 32 * qb + 16 * (nx % 2), nx / 2, lane);
         }
-        mma_a<T>(acc_v[db], ta[k & 1], pf[u]);
-        mma_a<T>(acc_k[db], tb[k & 1], dsf[u]);
+        mma_a<T>(acc_v[db], ta[k % 3], pf[u]);
+        mma_a<T>(acc_k[db], tb[k % 3], dsf[u]);
         __builtin_amdgcn_sched_barrier(0);
       });
       // every accumulation complete before the compiler may move an
