@@ -44,10 +44,18 @@ constexpr int kPage = 16;
 constexpr float kRescaleThreshold = 8.f;  // log2 units
 
 // Chunk permutation of K row t in a staging slot (VCH 16-byte chunks per
-// row): 16 consecutive rows read at one logical chunk land on 16 distinct
-// 16-byte bank groups.
+// row), XOR-ed onto the chunk index: 16 consecutive rows read at one logical
+// chunk land on 16 distinct 16-byte bank groups. The score operand read
+// (ds_read_b128: lane l reads row l%16 at logical chunk c0 + (l/16) *
+// (VCH/4)) is free of bank conflicts on gfx950 only when the chunk bit that
+// the lane group l/16 steps through is XOR-ed with a low row bit (row bit 0
+// or 1 at 256-byte rows; bit 1 at 128-byte rows, where bit 0 picks the bank
+// half): the plain t & 15 (or (t >> 1) & 7) costs four conflict cycles per
+// read, measured with SQ_LDS_BANK_CONFLICT. Hence row bits 1 and 2 trade
+// places (d = 128), and bits 1 and 2 of t >> 1 do (d = 64).
 template <int VCH> __device__ __forceinline__ int kswz(int t) {
-  return VCH == 16 ? (t & 15) : ((t >> 1) & 7);
+  return VCH == 16 ? ((t & 9) | ((t & 2) << 1) | ((t & 4) >> 1))
+                   : ((((t >> 3) & 1) << 2) | (t & 2) | ((t >> 2) & 1));
 }
 
 template <typename T> struct Mma16;
