@@ -20,6 +20,10 @@ it.
 The CPU baseline is the fp64 oracle run on a bounded sample of the same
 prefill workload (whole heads, every row) on this host's cores.
 
+``roofline.gemm_bf16_ceiling`` is the sustained rate of the vendor bf16
+GEMM on random operands in the same process: the matrix-core rate the board
+actually holds under its power limit, for comparison with the datasheet peak.
+
 ``roofline.traffic`` is the HBM bytes per call from rocprofv3 FETCH_SIZE and
 WRITE_SIZE counters calibrated on a copy of known size, as recorded in
 profiles/hbm_traffic.txt; it is null when the kernel sources no longer
@@ -351,6 +355,37 @@ def other_configs(torch, fa, fi, to_dev, dev, reps=20):
     return res
 
 
+def gemm_ceiling(torch, dev, seconds=2.0, n=8192):
+    """Sustained rate of the vendor bf16 GEMM (torch.matmul, which calls
+    hipBLASLt) on N(0,1) operands, M = N = K = n, run back to back for about
+    `seconds` in this process: the dense bf16 matrix-core rate this board
+    holds under its power limit, reported next to the datasheet peak."""
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16).contiguous()
+    b = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16).contiguous()
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(5):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    calls = max(10, int(seconds * 1e3 / (e0.elapsed_time(e1) / 10)))
+    e0.record()
+    for _ in range(calls):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"kernel": f"torch.matmul bf16 (hipBLASLt) M=N=K={n}, N(0,1) operands",
+            "calls": calls, "ms_per_call": ms, "tflops": tflops,
+            "frac_of_datasheet": tflops / PEAK_BF16_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,6 +398,8 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the throughput report of the other parity workloads")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the sustained vendor bf16 GEMM rate reported beside the prefill roofline")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, copy this many MiB device-to-device once (a kernel of "
                          "known traffic, to calibrate HBM byte counters)")
@@ -493,6 +530,11 @@ def main():
                          "traffic": tr_dec["bytes_per_call"] if tr_dec else None,
                          "kernel": "decode_split_kernel + decode_combine_kernel"},
         }
+    if do_pre and not args.no_ceiling:
+        log("[bench] sustained bf16 GEMM rate (matrix-core ceiling under the power limit)")
+        ceil = gemm_ceiling(torch, dev)
+        ceil["prefill_frac_of_gemm"] = out["value"] / ceil["tflops"]
+        out["roofline"]["gemm_bf16_ceiling"] = ceil
     parity_ok = True
     if not args.no_check:
         out["parity"] = {}
