@@ -20,9 +20,12 @@ it.
 The CPU baseline is the fp64 oracle run on a bounded sample of the same
 prefill workload (whole heads, every row) on this host's cores.
 
-``roofline.gemm_bf16_ceiling`` is the sustained rate of the vendor bf16
-GEMM on random operands in the same process: the matrix-core rate the board
-actually holds under its power limit, for comparison with the datasheet peak.
+``roofline.sustained_prefill`` and ``roofline.gemm_bf16_ceiling`` are the
+prefill and the vendor bf16 GEMM (random operands) each run back to back for
+a few seconds after the timed steps, with the board's power and GFX clocks
+read once by amd-smi halfway through: the rates the board holds under its
+power limit, as fractions of the datasheet peak and of the peak at the
+sampled clock.
 
 ``roofline.traffic`` is the HBM bytes per call from rocprofv3 FETCH_SIZE and
 WRITE_SIZE counters calibrated on a copy of known size, as recorded in
@@ -45,6 +48,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s (prefill) & KV GB/s (paged decode), % of MI355X peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_CLOCK_MHZ = 2400.0     # the engine clock the bf16 peak is quoted at
 
 
 def log(*a):
@@ -355,35 +359,77 @@ def other_configs(torch, fa, fi, to_dev, dev, reps=20):
     return res
 
 
+def board_sample():
+    """The board's socket power (W) and the GFX clock of each XCD (MHz), read
+    once with amd-smi; None when amd-smi is missing or prints no clocks."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "-g", "0"], capture_output=True,
+                           text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    clks = [int(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", r.stdout)]
+    if not clks:
+        return None
+    pw = re.search(r"SOCKET_POWER:\s*([\d.]+)\s*W", r.stdout)
+    return {"socket_power_w": float(pw.group(1)) if pw else None, "gfx_clock_mhz": clks,
+            "mean_gfx_clock_mhz": sum(clks) / len(clks)}
+
+
+def sustained(torch, fn, flops, seconds):
+    """Runs fn back to back for about `seconds`, reading the board's power
+    and clocks once halfway through: the rate a kernel holds under the
+    board's power limit, and the clock it holds it at. The matrix-core peak
+    at that clock is the datasheet peak scaled by clock / 2.4 GHz."""
+    import threading
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    calls = max(10, int(seconds * 1e3 / (e0.elapsed_time(e1) / 5)))
+    box = {}
+
+    def sample():
+        time.sleep(seconds / 2)
+        box["board"] = board_sample()
+
+    th = threading.Thread(target=sample)
+    th.start()
+    e0.record()
+    for _ in range(calls):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    th.join()
+    ms = e0.elapsed_time(e1) / calls
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {"calls": calls, "ms_per_call": ms, "tflops": tflops,
+           "frac_of_datasheet": tflops / PEAK_BF16_TFLOPS, "board": box.get("board")}
+    if out["board"]:
+        clk_peak = PEAK_BF16_TFLOPS * out["board"]["mean_gfx_clock_mhz"] / PEAK_CLOCK_MHZ
+        out["clock_peak_tflops"] = clk_peak
+        out["frac_of_clock_peak"] = tflops / clk_peak
+    return out
+
+
 def gemm_ceiling(torch, dev, seconds=2.0, n=8192):
     """Sustained rate of the vendor bf16 GEMM (torch.matmul, which calls
-    hipBLASLt) on N(0,1) operands, M = N = K = n, run back to back for about
-    `seconds` in this process: the dense bf16 matrix-core rate this board
-    holds under its power limit, reported next to the datasheet peak."""
+    hipBLASLt) on N(0,1) operands, M = N = K = n: the dense bf16 matrix-core
+    rate this board holds under its power limit, reported next to the
+    datasheet peak."""
     g = torch.Generator(device=dev).manual_seed(0)
     a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16).contiguous()
     b = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16).contiguous()
     c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for _ in range(5):
-        torch.matmul(a, b, out=c)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(10):
-        torch.matmul(a, b, out=c)
-    e1.record()
-    torch.cuda.synchronize()
-    calls = max(10, int(seconds * 1e3 / (e0.elapsed_time(e1) / 10)))
-    e0.record()
-    for _ in range(calls):
-        torch.matmul(a, b, out=c)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / calls
-    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
-    return {"kernel": f"torch.matmul bf16 (hipBLASLt) M=N=K={n}, N(0,1) operands",
-            "calls": calls, "ms_per_call": ms, "tflops": tflops,
-            "frac_of_datasheet": tflops / PEAK_BF16_TFLOPS}
+    res = sustained(torch, lambda: torch.matmul(a, b, out=c), 2.0 * n ** 3, seconds)
+    res["kernel"] = f"torch.matmul bf16 (hipBLASLt) M=N=K={n}, N(0,1) operands"
+    return res
 
 
 def main():
@@ -531,6 +577,11 @@ def main():
                          "kernel": "decode_split_kernel + decode_combine_kernel"},
         }
     if do_pre and not args.no_ceiling:
+        log("[bench] prefill held back to back for 3 s, board power and clocks sampled")
+        burst = sustained(torch, lambda: fa.fwd(q, k, v, causal=True, scale=x.scale, out=o, lse=lse),
+                          pre_flops, 3.0)
+        burst["kernel"] = "fwd_mfma_kernel<Bf16,128,causal>, the timed workload"
+        out["roofline"]["sustained_prefill"] = burst
         log("[bench] sustained bf16 GEMM rate (matrix-core ceiling under the power limit)")
         ceil = gemm_ceiling(torch, dev)
         ceil["prefill_frac_of_gemm"] = out["value"] / ceil["tflops"]
