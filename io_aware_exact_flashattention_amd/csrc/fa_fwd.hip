@@ -43,7 +43,10 @@
 //    round-robin over the XCDs, keeping that K/V in one XCD's L2, and each
 //    XCD runs its query tiles longest (last, under a causal mask) first.
 //  * Causal: K/V tiles that no row of the Q tile may see are never loaded;
-//    only tiles that cross the diagonal or the sequence end are masked.
+//    only tiles that cross the diagonal or the sequence end are masked. A
+//    wave skips the computation of the tiles that none of its own rows may
+//    see (and a wave whose rows all lie past the sequence end computes
+//    nothing), passing only their barriers.
 //
 // fp32 inputs take fwd_f32_kernel: the same fused pass on the fp32 matrix
 // cores (v_mfma_f32_32x32x2_f32), fp32 throughout, with the key range of a
@@ -203,6 +206,16 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
 
   const int wrow0 = row0 + wave * 32;
   const int my_row = wrow0 + l32;
+  // Key tiles that some row of this wave can see: none when every row lies
+  // past the sequence end, and under the causal mask none past the wave's
+  // last row. The later tiles of the workgroup add exactly nothing to this
+  // wave's rows (weights 0, running max unchanged), so the wave skips their
+  // softmax and products and only passes their barriers (with its share of
+  // the tile loads).
+  int kv_end_w = wrow0 < Lq ? Lk : 0;
+  if (CAUSAL) kv_end_w = min(kv_end_w, wrow0 + 32 + delta);
+  const int n_kv_w =
+      __builtin_amdgcn_readfirstlane(kv_end_w > 0 ? (kv_end_w + kBN - 1) / kBN : 0);
 
   if (n_kv == 0) {  // no row of the tile sees a key: O = 0, LSE = -inf
     if (my_row < Lq) {
@@ -486,6 +499,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   };
 
   auto scores0 = [&]() {
+    if (n_kv_w == 0) return;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -525,9 +539,11 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
     }
   };
   // Each group runs its own loop; both pass barriers 0 .. 2 n_kv in order.
+  // A wave works on tiles 0 .. n_kv_w - 1 and only passes the barriers of
+  // the rest.
   if (grp == 0) {
     barrier(0);
-    for (int j = 0; j < n_kv; ++j) {
+    for (int j = 0; j < n_kv_w; ++j) {
       softmax(j);     // slot 2j
       barrier(2 * j + 1);
       matrix(j);      // slot 2j+1
@@ -536,12 +552,16 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   } else {
     barrier(0);
     scores0();        // slot 0
-    for (int j = 0; j < n_kv; ++j) {
+    for (int j = 0; j < n_kv_w; ++j) {
       barrier(2 * j + 1);
       softmax(j);     // slot 2j+1
       barrier(2 * j + 2);
       matrix(j);      // slot 2j+2
     }
+  }
+  for (int j = n_kv_w; j < n_kv; ++j) {
+    barrier(2 * j + 1);
+    barrier(2 * j + 2);
   }
 
   // ---- epilogue: O = O / l, LSE = ln(sum exp) ----
