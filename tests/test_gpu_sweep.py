@@ -1,4 +1,5 @@
-"""Seeded random sweep of shapes against the fp64 oracle: ragged batches,
+"""Seeded random sweep of shapes against the fp64 oracles (forward and
+backward): ragged batches,
 query-head groups of every size the kernels specialise for (and odd ones),
 head dims 64/128, bf16/fp16, causal or not, lengths on and off the 16-token
 page, 32-row wave and 128/256-row tile boundaries, more queries than keys.
@@ -8,6 +9,7 @@ import numpy as np
 import pytest
 
 import fa_inputs as fi
+from tests import test_gpu_backward as tbwd
 from tests import test_gpu_decode as tdec
 from tests import test_gpu_paged_prefill as tpp
 from tests import test_gpu_prefill as tpre
@@ -84,3 +86,21 @@ def test_sweep_decode(case):
     x = fi.paged(lens, Hq, Hkv, d, dtype, seed=9000 + case)
     tdec.check(x, f"sweep decode #{case}: B={B} Hq={Hq} Hkv={Hkv} d={d} {dtype} lens={lens}",
                num_splits=num_splits)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_sweep_backward(case):
+    rng = np.random.default_rng(9500 + case)
+    B = int(rng.integers(1, 3))
+    Hq, Hkv = draw_heads(rng)
+    Hq, Hkv = min(Hq, 12), min(Hkv, 12)
+    while Hq % Hkv:
+        Hkv -= 1
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "f16"]))
+    causal = bool(rng.random() < 0.6)
+    nq = max(1, draw_len(rng, 400))
+    nk = nq if rng.random() < 0.5 else max(1, draw_len(rng, 400))
+    x = fi.dense(B, nq, nk, Hq, Hkv, d, dtype, seed=9500 + case, causal=causal)
+    tbwd.check_dense(x, f"sweep bwd #{case}: B={B} Hq={Hq} Hkv={Hkv} d={d} {dtype} "
+                        f"causal={causal} nq={nq} nk={nk}", 9500 + case)
