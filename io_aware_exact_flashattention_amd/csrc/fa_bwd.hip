@@ -19,16 +19,22 @@
 //    vectors as MFMA B operands held in registers (a lane owns one query
 //    row), then dS^T, then dQ^T += K^T dS^T with K^T read transposed from the
 //    K tile. It also writes D of its rows to the workspace.
-//  * bwd_dkdv_kernel: a workgroup owns 128 keys of one key/value head (4
-//    waves x 32 keys), K and V of those keys held in registers, and streams
-//    the Q/dO tiles (with their lse and D) of every query head of the group
-//    through LDS. Per 32-row block it forms S = Q K^T and dP = dO V^T (a
-//    lane owns one key), P and dS, then dV^T += dO^T P and dK^T += Q^T dS
-//    with dO^T and Q^T read transposed from the tiles. At d = 128 a wave
-//    runs its blocks as a two-stage pipeline: the score MFMAs of the next
-//    block are interleaved with the softmax of the current one.
-// Tiles reach LDS by direct-to-LDS copies; S and dP live in VGPRs and the
-// gradient accumulators in AGPRs (inline-asm MFMAs with explicit waits).
+//  * dK/dV: a workgroup owns 128 keys of one key/value head, K and V of
+//    those keys held in registers, and streams the Q/dO tiles (with their
+//    lse and D) of every query head of the group through LDS. Per 32-row
+//    block it forms S = Q K^T and dP = dO V^T (a lane owns one key), P and
+//    dS, then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
+//    transposed from the tiles. At d = 128 (bwd_dkdv_pair_kernel) two waves
+//    of a SIMD share each 32-key group: one forms S, P and dV, the other dP,
+//    dS and dK, with P passed through LDS, in counter-phase like the
+//    forward kernel's wave pairs. At d = 64 (bwd_dkdv_kernel) one wave does
+//    all of it for its 32 keys, so that two workgroups fit on a CU.
+// Work items are numbered so that each XCD runs a contiguous stretch of the
+// work list: the items running on one XCD at a time read the same Q/dO (or
+// K/V) tiles, which then stay in its L2.
+// Tiles reach LDS by direct-to-LDS copies; S and dP live in VGPRs, the
+// gradient accumulators in AGPRs or VGPRs (inline-asm MFMAs with fixed
+// register classes and explicit waits).
 // The score and probability fragments of one product are the B operands of
 // the next: in a 32x32 MFMA result lane l holds column l % 32 and rows
 // 8(r/4) + 4(l/32) + r%4 of its 16 registers r, so registers 8u .. 8u+7
@@ -50,7 +56,6 @@ constexpr int kDqRows = 128;      // query rows per workgroup of the dQ kernel
 constexpr int kDqKeys = 64;       // keys per K/V tile of the dQ kernel
 constexpr int kKvKeys = 128;      // keys per workgroup of the dK/dV kernel
 constexpr int kKvRows = 64;       // query rows per Q/dO tile of the dK/dV kernel
-constexpr int kRing = 3;          // LDS buffers of the dK/dV kernel's Q/dO tile ring (d = 128)
 
 // Calls f(std::integral_constant<int, i>) for i = I .. N-1: the index is a
 // constant expression in the body.
@@ -61,11 +66,6 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<I + 1, N>(f);
   }
 }
-// Keep a value's computation ahead of this point (an empty volatile asm
-// uses it; the compiler does not move volatile asm across the scheduling
-// fences that lay out the MFMA/softmax interleave).
-__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
 typedef short b_s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) b_s16x4 b_lds_s16x4;
@@ -133,19 +133,19 @@ struct Tile {
 // permutation puts there. Rows at or past `valid` repeat row valid - 1:
 // the callers give their products a zero weight (masked keys; query rows
 // with P = 0).
-template <int D, int ROWS>
+template <int D, int ROWS, int THREADS = kBwdThreads>
 struct TileCopy {
   static constexpr int CH = D / 8;
-  static constexpr int N = ROWS * CH / kBwdThreads;  // loads per thread
-  static_assert(N * kBwdThreads == ROWS * CH, "tile pieces");
+  static constexpr int N = ROWS * CH / THREADS;  // loads per thread
+  static_assert(N * THREADS == ROWS * CH, "tile pieces");
   __device__ static __forceinline__ void issue(const uint16_t* base, int64_t stride, int row0,
                                                int valid, uint32_t lds_tile, int wave, int lane) {
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      const int idx = n * kBwdThreads + wave * 64 + lane, row = idx / CH;
+      const int idx = n * THREADS + wave * 64 + lane, row = idx / CH;
       const int c = (idx % CH) ^ Tile<D>::swz(row);
       const int r = min(row0 + row, valid - 1);
-      load_to_lds(base + (int64_t)r * stride + 8 * c, lds_tile + 16 * (n * kBwdThreads + wave * 64));
+      load_to_lds(base + (int64_t)r * stride + 8 * c, lds_tile + 16 * (n * THREADS + wave * 64));
     }
   }
 };
@@ -200,16 +200,6 @@ __device__ __forceinline__ void wait_operands(uint4 (&a)[2], uint4 (&b)[2]) {
   b[0] = __builtin_bit_cast(uint4, y0);
   b[1] = __builtin_bit_cast(uint4, y1);
 }
-// the same for two accumulator sets
-template <int DB>
-__device__ __forceinline__ void wait_acc2(f32x16 (&a)[DB], f32x16 (&b)[DB]) {
-  if constexpr (DB == 4)
-    asm volatile("s_nop 15\n\ts_nop 2"
-                 : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(b[0]), "+a"(b[1]),
-                   "+a"(b[2]), "+a"(b[3]));
-  else
-    asm volatile("s_nop 15\n\ts_nop 2" : "+a"(a[0]), "+a"(a[1]), "+a"(b[0]), "+a"(b[1]));
-}
 // 19 wait states after the last accumulation, before the epilogue reads the
 // accumulators
 template <int DB>
@@ -218,6 +208,15 @@ __device__ __forceinline__ void wait_acc(f32x16 (&a)[DB]) {
     asm volatile("s_nop 15\n\ts_nop 2" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
   else
     asm volatile("s_nop 15\n\ts_nop 2" : "+a"(a[0]), "+a"(a[1]));
+}
+
+// the same for accumulators held in VGPRs
+template <int DB>
+__device__ __forceinline__ void wait_acc_v(f32x16 (&a)[DB]) {
+  if constexpr (DB == 4)
+    asm volatile("s_nop 15\n\ts_nop 2" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+  else
+    asm volatile("s_nop 15\n\ts_nop 2" : "+v"(a[0]), "+v"(a[1]));
 }
 
 // sum of the products of the eight 16-bit values of a and b, in fp32
@@ -229,6 +228,16 @@ __device__ __forceinline__ float dot8(uint4 a, uint4 b) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) s = fmaf(E::lo(wa[i]), E::lo(wb[i]), fmaf(E::hi(wa[i]), E::hi(wb[i]), s));
   return s;
+}
+
+// Workgroups are dealt round-robin over the 8 XCDs (workgroup L runs on
+// XCD L % 8); this renumbering gives XCD x the contiguous range
+// [x*per + min(x, rem), ...) of the work list, so that the items running on
+// one XCD at a time are neighbours in the list and share tiles in its L2.
+__device__ __forceinline__ int xcd_item() {
+  const int L = blockIdx.x, total = gridDim.x;
+  const int xcd = L & 7, per = total >> 3, rem = total & 7;
+  return xcd * per + min(xcd, rem) + (L >> 3);
 }
 
 // lse (natural log) -> the log2-domain offset of P = exp2(s * scale_log2 -
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdParams p) {
 
   // work item (sequence b, query head h, query tile t), longest causal tiles first
   const int nt = (p.Nq + kDqRows - 1) / kDqRows;
-  int idx = blockIdx.x;
+  int idx = xcd_item();
   const int t = nt - 1 - idx % nt;
   idx /= nt;
   const int h = idx % p.Hq, b = idx / p.Hq;
@@ -376,20 +385,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdParams p) {
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
+  static_assert(D == 64, "d = 128 runs bwd_dkdv_pair_kernel");
   using E = Elem<T>;
   using G = Tile<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int QB = kKvRows / 32;  // 32-row blocks per Q/dO tile
   constexpr int TB = kKvRows * G::ROWB;
-  constexpr int RING = D == 128 ? kRing : 2;
+  constexpr int RING = 2;
   __shared__ __attribute__((aligned(16))) char lds[RING][2][TB];  // [buffer][Q, dO]
   __shared__ __attribute__((aligned(16))) float lds_r[RING][2][kKvRows];  // [buffer][offset, D]
 
   // work item (sequence b, key/value head g, key tile t); under a causal
   // mask the first key tiles see the most queries and come first
   const int nt = (p.Nk + kKvKeys - 1) / kKvKeys;
-  int idx = blockIdx.x;
+  int idx = xcd_item();
   const int t = idx % nt;
   idx /= nt;
   const int g = idx % p.Hkv, b = idx / p.Hkv;
@@ -430,11 +440,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_k[db][r] = acc_v[db][r] = 0.f;
 
-  // Q/dO tiles go through a ring of RING LDS buffers: the barrier opening
-  // tile it issues the copies of tile it + 1 into the buffer of tile
-  // it + 1 - RING, whose last reads every wave has finished by then (with
-  // the pipeline below, the gradients of tile it - 1 still read their
-  // buffer after that barrier, hence three buffers at d = 128).
+  // Q/dO tiles alternate between two LDS buffers: the barrier opening tile
+  // it issues the copies of tile it + 1 into the other buffer, whose last
+  // reads (tile it - 1) every wave has finished by then.
   const uint32_t lds0 = lds_address(lds);
   using Copy = TileCopy<D, kKvRows>;
   float sr = 0.f;  // thread tid < 2*kKvRows stages one lse offset or D value
@@ -452,211 +460,66 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
       else sr = row < Lq ? p.dsum[li] : 0.f;
     }
   };
-  auto open_tile = [&](int it) {
-    if (tid < 2 * kKvRows) lds_r[it % RING][tid / kKvRows][tid % kKvRows] = sr;
+  // one 32-row block after the other
+  if (n_it > 0) load(0);
+  for (int it = 0; it < n_it; ++it) {
+    const int buf = it % RING;
+    // Q/dO tile it complete everywhere; tile it + 1 goes to the other
+    // buffer, last read in iteration it - 1, before every thread passed
+    // this barrier
+    if (tid < 2 * kKvRows) lds_r[buf][tid / kKvRows][tid % kKvRows] = sr;
     wait_tile_copies();
     __syncthreads();
-    if (it + 1 < n_it) load(it + 1);
-  };
-  auto qtile = [&](int it) { return (b_lds_cchar*)lds[it % RING][0]; };
-  auto dotile = [&](int it) { return (b_lds_cchar*)lds[it % RING][1]; };
-
-  // The 32-row blocks m = QB it + qb run as a pipeline in one wave: slot m
-  // issues the 16 score MFMAs of block m + 1 (S = Q K^T, dP = dO V^T; lane
-  // = key), each followed by one element of block m's softmax (P and
-  // dS = P o (dP - D) for one query row), then the 16 gradient MFMAs of
-  // block m (dV^T += dO^T P, dK^T += Q^T dS). The matrix core then has the
-  // next block's MFMAs to run while the vector ALUs work on the current
-  // block. Scores alternate between two register sets by block parity.
-  f32x16 sA, dA, sB, dB;
-  // scores of block (it, qb) into (sn, dn), each MFMA followed by element
-  // j of the softmax of the block (itc, qbc) in (sc, dc) when soft is set
-  auto slot = [&](int it, int qb, f32x16& sc, f32x16& dc, f32x16& sn, f32x16& dn, int itn,
-                  int qbn, auto next_c, auto soft_c) {
-    constexpr bool has_next = decltype(next_c)::value;
-    constexpr bool soft = decltype(soft_c)::value;
-    b_lds_cchar* Qn = qtile(itn);
-    b_lds_cchar* dOn = dotile(itn);
-    const int buf = it % RING;
     const int q0 = (qt0 + it % n_qt) * kKvRows;
-    // register r holds query row q0 + 32 qb + 4 hh + 8 (r/4) + r%4 of this
-    // key; under the causal mask it is visible iff 8 (r/4) + r%4 >= thr
-    const int thr = my_key - delta - (q0 + 32 * qb + 4 * hh);
-    float pe0 = 0.f, de0 = 0.f;
-    uint32_t pw[8], dw[8];  // P and dS of the block, packed to 16 bits
-    // the block's lse offsets and D values, read before its 16 steps so that
-    // their LDS latency is not waited out inside them
-    float ov[16], dv[16];
-    if constexpr (soft) {
+    if (it + 1 < n_it) load(it + 1);
+    b_lds_cchar* Q = (b_lds_cchar*)lds[buf][0];
+    b_lds_cchar* dO = (b_lds_cchar*)lds[buf][1];
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int rb = 32 * qb + 8 * gq + 4 * hh;  // first of four rows
-        const float4 o4 = *(const float4*)&lds_r[buf][0][rb];
-        const float4 d4 = *(const float4*)&lds_r[buf][1][rb];
-        ov[4 * gq] = o4.x; ov[4 * gq + 1] = o4.y; ov[4 * gq + 2] = o4.z; ov[4 * gq + 3] = o4.w;
-        dv[4 * gq] = d4.x; dv[4 * gq + 1] = d4.y; dv[4 * gq + 2] = d4.z; dv[4 * gq + 3] = d4.w;
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 st, dp;
+      mma_v0<T>(st, G::row_frag(Q, 32 * qb, 0, lane), kf[0]);
+      mma_v0<T>(dp, G::row_frag(dO, 32 * qb, 0, lane), vf[0]);
+#pragma unroll
+      for (int s = 1; s < KS; ++s) {
+        mma_v<T>(st, G::row_frag(Q, 32 * qb, s, lane), kf[s]);
+        mma_v<T>(dp, G::row_frag(dO, 32 * qb, s, lane), vf[s]);
       }
-    }
-    // score fragments read AHEAD MFMAs ahead of their use, in a ring of
-    // AHEAD + 1 register sets (one MFMA plus one softmax element covers
-    // only a fraction of an LDS read's latency)
-    constexpr int AHEAD = 3;
-    uint4 fr[AHEAD + 1];
-    // 16 steps, one softmax element each; the 2 KS score MFMAs go to every
-    // STEP-th step (MFMA mi: k-step mi / 2, S for even mi, dP for odd)
-    constexpr int STEP = 16 / (2 * KS);
-    static_assert(STEP * 2 * KS == 16, "score MFMAs per block");
-    if constexpr (has_next)
-      static_for<0, AHEAD>([&](auto m_c) {
-        constexpr int m = decltype(m_c)::value;
-        if constexpr (m < 2 * KS) fr[m] = G::row_frag((m & 1) ? dOn : Qn, 32 * qbn, m / 2, lane);
-      });
-    static_for<0, 16>([&](auto j_c) {
-      constexpr int j = decltype(j_c)::value;
-      if constexpr (has_next && j % STEP == 0) {
-        constexpr int mi = j / STEP, s = mi / 2, nx = mi + AHEAD;
-        if constexpr (nx < 2 * KS)
-          fr[nx % (AHEAD + 1)] = G::row_frag((nx & 1) ? dOn : Qn, 32 * qbn, nx / 2, lane);
-        constexpr int fi = mi % (AHEAD + 1);
-        if constexpr (mi & 1) {
-          if constexpr (s == 0) mma_v0<T>(dn, fr[fi], vf[0]);
-          else mma_v<T>(dn, fr[fi], vf[s]);
-        } else {
-          if constexpr (s == 0) mma_v0<T>(sn, fr[fi], kf[0]);
-          else mma_v<T>(sn, fr[fi], kf[s]);
+      wait_scores(st, dp);
+      // register r holds query row q0 + 32 qb + 4 hh + 8 (r/4) + r%4 of this key;
+      // under the causal mask it is visible iff 8 (r/4) + r%4 >= thr
+      const int thr = my_key - delta - (q0 + 32 * qb + 4 * hh);
+      uint4 pf[2], dsf[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float pe[8], de[8];
+#pragma unroll
+        for (int gq = 0; gq < 2; ++gq) {
+          const int rb = 32 * qb + 8 * (2 * u + gq) + 4 * hh;  // first of four rows
+          const float4 o4 = *(const float4*)&lds_r[buf][0][rb];
+          const float4 d4 = *(const float4*)&lds_r[buf][1][rb];
+          const float ov[4] = {o4.x, o4.y, o4.z, o4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 8 * u + 4 * gq + i;
+            const bool vis = !CAUSAL || (8 * (r >> 2) + (r & 3) >= thr);
+            const float pv = vis ? fast_exp2(fmaf(st[r], c2, -ov[i])) : 0.f;
+            pe[4 * gq + i] = pv;
+            de[4 * gq + i] = pv * (dp[r] - dv[i]);
+          }
         }
+        pf[u] = make_uint4(E::pack2(pe[0], pe[1]), E::pack2(pe[2], pe[3]), E::pack2(pe[4], pe[5]),
+                           E::pack2(pe[6], pe[7]));
+        dsf[u] = make_uint4(E::pack2(de[0], de[1]), E::pack2(de[2], de[3]),
+                            E::pack2(de[4], de[5]), E::pack2(de[6], de[7]));
       }
-      if constexpr (soft) {
-        constexpr int r = j, gq = r / 4, i = r % 4;
-        const bool vis = !CAUSAL || (8 * gq + i >= thr);
-        float e = fast_exp2(fmaf(sc[r], c2, -ov[r]));
-        pin(e);  // computed for every lane, then selected: no branch
-        const float pv = vis ? e : 0.f;
-        const float dsv = pv * (dc[r] - dv[r]);
-        if constexpr (r % 2 == 0) {
-          pe0 = pv;
-          de0 = dsv;
-        } else {  // registers r - 1, r: one 32-bit word of each operand
-          pw[r / 2] = E::pack2(pe0, pv);
-          dw[r / 2] = E::pack2(de0, dsv);
-          pin(pw[r / 2]);
-          pin(dw[r / 2]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    if constexpr (has_next) wait_scores(sn, dn);
-    if constexpr (soft) {
-      uint4 pf[2] = {make_uint4(pw[0], pw[1], pw[2], pw[3]), make_uint4(pw[4], pw[5], pw[6], pw[7])};
-      uint4 dsf[2] = {make_uint4(dw[0], dw[1], dw[2], dw[3]), make_uint4(dw[4], dw[5], dw[6], dw[7])};
       wait_operands(pf, dsf);
-      b_lds_cchar* Q = qtile(it);
-      b_lds_cchar* dO = dotile(it);
-      // transposed fragments two MFMA pairs ahead, in a ring of three
-      uint4 ta[3], tb[3];
-      static_for<0, 2>([&](auto m_c) {
-        constexpr int m = decltype(m_c)::value;
-        ta[m] = G::tr_frag(dO, 32 * qb + 16 * (m % 2), m / 2, lane);
-        tb[m] = G::tr_frag(Q, 32 * qb + 16 * (m % 2), m / 2, lane);
-      });
-      static_for<0, 2 * DB>([&](auto k_c) {
-        constexpr int k = decltype(k_c)::value, db = k / 2, u = k % 2, nx = k + 2;
-        if constexpr (nx < 2 * DB) {
-          ta[nx % 3] = G::tr_frag(dO, 32 * qb + 16 * (nx % 2), nx / 2, lane);
-          tb[nx % 3] = G::tr_frag(Q, 32 * qb + 16 * (nx % 2), nx / 2, lane);
-        }
-        mma_a<T>(acc_v[db], ta[k % 3], pf[u]);
-        mma_a<T>(acc_k[db], tb[k % 3], dsf[u]);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      // every accumulation complete before the compiler may move an
-      // accumulator for its own register allocation
-      wait_acc2<DB>(acc_v, acc_k);
-    }
-  };
-
-  std::integral_constant<bool, true> yes;
-  std::integral_constant<bool, false> no;
-  static_assert(QB == 2, "two blocks per tile");
-  if constexpr (D == 128) {
-    if (n_it > 0) {
-      load(0);
-      open_tile(0);
-      slot(0, 0, sA, dA, sA, dA, 0, 0, yes, no);  // scores of block 0 only
-      for (int it = 0; it + 1 < n_it; ++it) {
-        // block (it, 0): the scores of (it, 1) come from the same tile
-        slot(it, 0, sA, dA, sB, dB, it, 1, yes, yes);
-        // block (it, 1): the scores of (it + 1, 0) need tile it + 1 opened
-        open_tile(it + 1);
-        slot(it, 1, sB, dB, sA, dA, it + 1, 0, yes, yes);
-      }
-      const int il = n_it - 1;
-      slot(il, 0, sA, dA, sB, dB, il, 1, yes, yes);
-      slot(il, 1, sB, dB, sA, dA, il, 0, no, yes);
-    }
-  } else {
-    // d = 64: the blocks one after the other (the pipeline's second score set
-    // would cost the second workgroup per CU that this variant otherwise has)
-    if (n_it > 0) load(0);
-    for (int it = 0; it < n_it; ++it) {
-      const int buf = it % RING;
-      // Q/dO tile it complete everywhere; tile it + 1 goes to the other
-      // buffer, last read in iteration it - 1, before every thread passed
-      // this barrier
-      if (tid < 2 * kKvRows) lds_r[buf][tid / kKvRows][tid % kKvRows] = sr;
-      wait_tile_copies();
-      __syncthreads();
-      const int q0 = (qt0 + it % n_qt) * kKvRows;
-      if (it + 1 < n_it) load(it + 1);
-      b_lds_cchar* Q = (b_lds_cchar*)lds[buf][0];
-      b_lds_cchar* dO = (b_lds_cchar*)lds[buf][1];
-  #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        f32x16 st, dp;
-        mma_v0<T>(st, G::row_frag(Q, 32 * qb, 0, lane), kf[0]);
-        mma_v0<T>(dp, G::row_frag(dO, 32 * qb, 0, lane), vf[0]);
-  #pragma unroll
-        for (int s = 1; s < KS; ++s) {
-          mma_v<T>(st, G::row_frag(Q, 32 * qb, s, lane), kf[s]);
-          mma_v<T>(dp, G::row_frag(dO, 32 * qb, s, lane), vf[s]);
-        }
-        wait_scores(st, dp);
-        // register r holds query row q0 + 32 qb + 4 hh + 8 (r/4) + r%4 of this key;
-        // under the causal mask it is visible iff 8 (r/4) + r%4 >= thr
-        const int thr = my_key - delta - (q0 + 32 * qb + 4 * hh);
-        uint4 pf[2], dsf[2];
-  #pragma unroll
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
         for (int u = 0; u < 2; ++u) {
-          float pe[8], de[8];
-  #pragma unroll
-          for (int gq = 0; gq < 2; ++gq) {
-            const int rb = 32 * qb + 8 * (2 * u + gq) + 4 * hh;  // first of four rows
-            const float4 o4 = *(const float4*)&lds_r[buf][0][rb];
-            const float4 d4 = *(const float4*)&lds_r[buf][1][rb];
-            const float ov[4] = {o4.x, o4.y, o4.z, o4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
-  #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 8 * u + 4 * gq + i;
-              const bool vis = !CAUSAL || (8 * (r >> 2) + (r & 3) >= thr);
-              const float pv = vis ? fast_exp2(fmaf(st[r], c2, -ov[i])) : 0.f;
-              pe[4 * gq + i] = pv;
-              de[4 * gq + i] = pv * (dp[r] - dv[i]);
-            }
-          }
-          pf[u] = make_uint4(E::pack2(pe[0], pe[1]), E::pack2(pe[2], pe[3]), E::pack2(pe[4], pe[5]),
-                             E::pack2(pe[6], pe[7]));
-          dsf[u] = make_uint4(E::pack2(de[0], de[1]), E::pack2(de[2], de[3]),
-                              E::pack2(de[4], de[5]), E::pack2(de[6], de[7]));
+          mma_a<T>(acc_v[db], G::tr_frag(dO, 32 * qb + 16 * u, db, lane), pf[u]);
+          mma_a<T>(acc_k[db], G::tr_frag(Q, 32 * qb + 16 * u, db, lane), dsf[u]);
         }
-        wait_operands(pf, dsf);
-  #pragma unroll
-        for (int db = 0; db < DB; ++db)
-  #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            mma_a<T>(acc_v[db], G::tr_frag(dO, 32 * qb + 16 * u, db, lane), pf[u]);
-            mma_a<T>(acc_k[db], G::tr_frag(Q, 32 * qb + 16 * u, db, lane), dsf[u]);
-          }
-      }
     }
   }
   wait_acc<DB>(acc_v);
@@ -667,6 +530,306 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// dK/dV with the work of a 32-key group split over two waves that share a
+// SIMD. The "P wave" holds K, forms S = Q K^T and P and accumulates
+// dV^T += dO^T P; the "dS wave" holds V, forms dP = dO V^T and
+// dS = P o (dP - D) and accumulates dK^T += Q^T dS. P goes from the one to
+// the other through LDS in fp32, so every value is the one the single-wave
+// kernel computes. Each wave alternates a matrix phase (MFMAs and LDS
+// fragment reads) with a vector phase (P, or dS), the two waves of a SIMD in
+// counter-phase, every phase boundary a workgroup barrier, as in the forward
+// kernel:
+//   first half of slot i:  P wave  S(i+1), dV(i)   |  dS wave  dS(i)
+//   second half of slot i: P wave  P(i+1)          |  dS wave  dP(i+1), dK(i)
+// where i is a 64-row Q/dO tile. Tile i is read in slots i-1 and i; the
+// barrier that ends slot i-2 completes it, the one that ends slot i-3 issues
+// its copies into a ring of three buffers.
+constexpr int kPairThreads = 512;  // 4 key groups x 2 roles
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kPairThreads) void bwd_dkdv_pair_kernel(BwdParams p) {
+  using E = Elem<T>;
+  using G = Tile<D>;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TB = kKvRows * G::ROWB;
+  constexpr int RING = 3;
+  constexpr int STEPS = 2 * KS;  // MFMAs of each kind per matrix phase (two 32-row blocks)
+  static_assert(2 * 2 * DB == STEPS, "score and gradient MFMAs pair up");
+  constexpr int LD = kKvRows * G::CH / kPairThreads;  // copies per thread per tensor and tile
+  static_assert(LD * kPairThreads == kKvRows * G::CH, "tile pieces");
+  __shared__ __attribute__((aligned(16))) char lds[RING][2][TB];          // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float lds_r[RING][2][kKvRows];  // [buffer][offset, D]
+  // P of the current tile, per key group: float4 w of lane l at [w][l]
+  __shared__ __attribute__((aligned(16))) float4 xch[4][8][64];
+
+  const int nt = (p.Nk + kKvKeys - 1) / kKvKeys;
+  int idx = xcd_item();
+  const int t = idx % nt;
+  idx /= nt;
+  const int g = idx % p.Hkv, b = idx / p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3;     // key group; waves kg and kg + 4 share a SIMD
+  const int role = wave >> 2;  // 0: S, P, dV; 1: dP, dS, dK
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int Lq = p.Nq, Lk = p.Nk, delta = Lk - Lq;
+  const int my_key = t * kKvKeys + kg * 32 + l32;
+  const bool key_ok = my_key < Lk;
+  const int64_t ktok = (int64_t)b * Lk + my_key;
+  const int64_t koff = ktok * p.kv_row + (int64_t)g * D;
+
+  // K (P wave) or V (dS wave) of this lane's key: the B operand of the
+  // wave's score product
+  uint4 bf[KS];
+  if (key_ok) {
+    const uint16_t* src = (const uint16_t*)(role == 0 ? p.k : p.v) + koff + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) bf[s] = *(const uint4*)(src + 16 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) bf[s] = make_uint4(0, 0, 0, 0);
+  }
+
+  const int q_first = CAUSAL ? max(0, t * kKvKeys - delta) : 0;
+  const int qt0 = q_first / kKvRows;
+  const int n_qt = Lq > qt0 * kKvRows ? (Lq + kKvRows - 1) / kKvRows - qt0 : 0;
+  const int n_it = n_qt * p.group;  // (query head of the group, query tile), head-major
+  const float c2 = p.scale_log2;
+
+  f32x16 acc[DB];  // dV^T (P wave) or dK^T (dS wave)
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  f32x16 sc[2];    // S or dP of the two 32-row blocks of a tile
+  uint4 op[2][2];  // P or dS of a tile, packed: B operands of the gradient MFMAs
+
+  // ---- tile copies: a wave-uniform base plus 32-bit lane offsets ----
+  // Copy n of thread tid fills LDS chunk n * 512 + tid of the tile with the
+  // logical chunk that the tile permutation puts there; rows past the
+  // sequence end repeat its last row (their P is 0).
+  int cp_row[LD], cp_col[LD];  // row inside the tile, byte offset inside the row
+#pragma unroll
+  for (int n = 0; n < LD; ++n) {
+    const int i = n * kPairThreads + tid, row = i / G::CH;
+    cp_row[n] = row;
+    cp_col[n] = 16 * ((i % G::CH) ^ G::swz(row));
+  }
+  const uint32_t lds0 = lds_address(lds);
+  float sr = 0.f;  // thread tid < 2*kKvRows stages one lse offset or D value
+  auto load = [&](int it) {
+    const int h = g * p.group + it / n_qt;
+    const int q0 = (qt0 + it % n_qt) * kKvRows;
+    const int64_t e0 = ((int64_t)b * Lq + q0) * p.q_row + (int64_t)h * D;
+    const uint16_t* qb = (const uint16_t*)p.q + e0;
+    const uint16_t* db = (const uint16_t*)p.dout + e0;
+    const int last = Lq - 1 - q0;  // last row of the tile inside the sequence
+    const uint32_t t0 = lds0 + __builtin_amdgcn_readfirstlane((it % RING) * 2 * TB) + wave * 1024;
+#pragma unroll
+    for (int n = 0; n < LD; ++n) {
+      const uint32_t vo = (uint32_t)(min(cp_row[n], last) * (int)p.q_row * 2 + cp_col[n]);
+      load_to_lds_sv(qb, vo, t0 + n * kPairThreads * 16);
+      load_to_lds_sv(db, vo, t0 + TB + n * kPairThreads * 16);
+    }
+    if (tid < 2 * kKvRows) {
+      const int row = q0 + (tid % kKvRows);
+      const int64_t li = ((int64_t)b * Lq + row) * p.Hq + h;
+      if (tid < kKvRows) sr = row < Lq ? lse_offset(p.lse[li]) : __builtin_inff();
+      else sr = row < Lq ? p.dsum[li] : 0.f;
+    }
+  };
+  // barrier that ends slot it: tile it + 2 (issued one slot earlier) is
+  // complete and its lse/D values staged; tile it + 3 goes to the buffer of
+  // tile it, last read in slot it
+  auto end_slot = [&](int it) {
+    if (it + 2 < n_it && tid < 2 * kKvRows)
+      lds_r[(it + 2) % RING][tid / kKvRows][tid % kKvRows] = sr;
+    wait_tile_copies();
+    __syncthreads();
+    if (it + 3 < n_it) load(it + 3);
+  };
+
+  // ---- per-lane LDS read offsets inside a tile (bytes) ----
+  // Score A operand, row-major: row 32 qb + l32, logical chunk 2 s + hh (the
+  // 32-row step leaves the permutation unchanged: an immediate offset).
+  int s_off[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) s_off[s] = G::chunk(l32, 2 * s + hh);
+  // Gradient A operand, transposed: for d-block db the rows 4 hh + (l%16)/4
+  // and 8 more, at granule 8 db + 4 ((l/16)%2) + l%4 (the 16-row steps of
+  // qb and u leave the permutation unchanged).
+  int g_off[DB][2];
+  {
+    const int i = lane & 15, row = 4 * hh + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int gran = 8 * db + 4 * ((lane >> 4) & 1) + (i & 3);
+      g_off[db][0] = row * G::ROWB + 16 * ((gran >> 1) ^ G::swz(row)) + 8 * (gran & 1);
+      g_off[db][1] = (row + 8) * G::ROWB + 16 * ((gran >> 1) ^ G::swz(row + 8)) + 8 * (gran & 1);
+    }
+  }
+  // byte offset of a tile's Q (tensor 0) or dO (tensor 1) inside lds, as a
+  // wave-uniform value (so that the fragment addresses stay lane offset +
+  // uniform base instead of one induction variable each)
+  auto tile_base = [&](int it, int tensor) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((it % RING) * 2 * TB + tensor * TB);
+  };
+  b_lds_cchar* const L = (b_lds_cchar*)lds;
+
+  // Matrix phase: the score product of tile it + 1 (NEXT) and the gradient
+  // product of tile it (GRAD), one MFMA of each per step; A fragments are
+  // read two steps ahead. Score MFMA i: block i / KS, k-step i % KS.
+  // Gradient MFMA i: block i / (2 DB), d-block (i % (2 DB)) / 2, rows
+  // 16 (i % 2) of the block (the order of the single-wave kernel).
+  // score A operand rows: Q (P wave) or dO (dS wave) of tile it + 1;
+  // gradient A operand: dO (P wave) or Q (dS wave) of tile it, transposed
+  auto sfrag = [&](int it, int i) {
+    return lds_row16(L + tile_base(it + 1, role) + s_off[i % KS] + 32 * (i / KS) * G::ROWB);
+  };
+  auto gfrag = [&](int it, int i) {
+    const uint32_t yb = tile_base(it, 1 - role);
+    const int r0 = 32 * (i / (2 * DB)) + 16 * (i % 2), db = (i % (2 * DB)) / 2;
+    const uint2 lo = lds_tr8(L + yb + g_off[db][0] + r0 * G::ROWB);
+    const uint2 hi = lds_tr8(L + yb + g_off[db][1] + r0 * G::ROWB);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
+  // fragment rings of the matrix phase; the first two of each are read
+  // ahead of the phase (pre_s, pre_g), while the vector phase runs when the
+  // tile is already complete
+  uint4 fs[3], fg[3];
+  auto pre_s = [&](int it) { fs[0] = sfrag(it, 0); fs[1] = sfrag(it, 1); };
+  auto pre_g = [&](int it) { fg[0] = gfrag(it, 0); fg[1] = gfrag(it, 1); };
+  auto matrix = [&](int it, auto next_c, auto grad_c) {
+    constexpr bool NEXT = decltype(next_c)::value;
+    constexpr bool GRAD = decltype(grad_c)::value;
+    __builtin_amdgcn_s_setprio(1);
+    static_for<0, STEPS>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      if constexpr (i + 2 < STEPS) {
+        if constexpr (NEXT) fs[(i + 2) % 3] = sfrag(it, i + 2);
+        if constexpr (GRAD) fg[(i + 2) % 3] = gfrag(it, i + 2);
+      }
+      if constexpr (NEXT) {
+        constexpr int qb = i / KS, s = i % KS;
+        if constexpr (s == 0) mma_v0<T>(sc[qb], fs[i % 3], bf[0]);
+        else mma_v<T>(sc[qb], fs[i % 3], bf[s]);
+      }
+      if constexpr (GRAD) {
+        constexpr int qb = i / (2 * DB), db = (i % (2 * DB)) / 2, u = i % 2;
+        mma_v<T>(acc[db], fg[i % 3], op[qb][u]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    __builtin_amdgcn_s_setprio(0);
+    if constexpr (NEXT) wait_scores(sc[0], sc[1]);
+    if constexpr (GRAD) wait_acc_v<DB>(acc);
+  };
+
+  const int q_lane = 4 * hh;  // first query row of this lane in each group of 8
+  // P wave, vector phase: P of tile it from its scores, to the exchange
+  // buffer (fp32) and to op (packed)
+  auto probs = [&](int it) {
+    const int buf = it % RING, q0 = (qt0 + it % n_qt) * kKvRows;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // register r holds query row q0 + 32 qb + 4 hh + 8 (r/4) + r%4 of this
+      // key; under the causal mask it is visible iff 8 (r/4) + r%4 >= thr
+      const int thr = my_key - delta - (q0 + 32 * qb + q_lane);
+      float pv[16];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const float4 o4 = *(const float4*)&lds_r[buf][0][32 * qb + 8 * gq + q_lane];
+        const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * gq + i;
+          const bool vis = !CAUSAL || (8 * gq + i >= thr);
+          const float e = fast_exp2(fmaf(sc[qb][r], c2, -ov[i]));
+          pv[r] = vis ? e : 0.f;
+        }
+        xch[kg][4 * qb + gq][lane] =
+            make_float4(pv[4 * gq], pv[4 * gq + 1], pv[4 * gq + 2], pv[4 * gq + 3]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        op[qb][u] = make_uint4(E::pack2(pv[8 * u], pv[8 * u + 1]), E::pack2(pv[8 * u + 2], pv[8 * u + 3]),
+                               E::pack2(pv[8 * u + 4], pv[8 * u + 5]),
+                               E::pack2(pv[8 * u + 6], pv[8 * u + 7]));
+    }
+    wait_operands(op[0], op[1]);
+  };
+  // dS wave, vector phase: dS of tile it from P (exchange buffer) and dP
+  auto grads = [&](int it) {
+    const int buf = it % RING;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float dsv[16];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const float4 d4 = *(const float4*)&lds_r[buf][1][32 * qb + 8 * gq + q_lane];
+        const float4 p4 = xch[kg][4 * qb + gq][lane];
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w}, pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dsv[4 * gq + i] = pv[i] * (sc[qb][4 * gq + i] - dv[i]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        op[qb][u] = make_uint4(E::pack2(dsv[8 * u], dsv[8 * u + 1]), E::pack2(dsv[8 * u + 2], dsv[8 * u + 3]),
+                               E::pack2(dsv[8 * u + 4], dsv[8 * u + 5]),
+                               E::pack2(dsv[8 * u + 6], dsv[8 * u + 7]));
+    }
+    wait_operands(op[0], op[1]);
+  };
+
+  std::integral_constant<bool, true> yes;
+  std::integral_constant<bool, false> no;
+  if (n_it > 0) {
+    load(0);
+    if (tid < 2 * kKvRows) lds_r[0][tid / kKvRows][tid % kKvRows] = sr;
+    wait_tile_copies();
+    __syncthreads();
+    if (n_it > 1) load(1);
+    if (role == 0) {
+      pre_s(-1);
+      matrix(-1, yes, no);  // S(0)
+      __syncthreads();
+      probs(0);
+      pre_g(0);
+      end_slot(-1);
+      for (int it = 0; it + 1 < n_it; ++it) {
+        pre_s(it);  // tile it + 1, complete since the last barrier
+        matrix(it, yes, yes);  // S(it+1), dV(it)
+        __syncthreads();
+        probs(it + 1);
+        pre_g(it + 1);
+        end_slot(it);
+      }
+      matrix(n_it - 1, no, yes);  // dV(last)
+      __syncthreads();
+    } else {
+      __syncthreads();
+      pre_s(-1);
+      matrix(-1, yes, no);  // dP(0)
+      end_slot(-1);
+      for (int it = 0; it + 1 < n_it; ++it) {
+        grads(it);
+        pre_s(it);
+        pre_g(it);
+        __syncthreads();
+        matrix(it, yes, yes);  // dP(it+1), dK(it)
+        end_slot(it);
+      }
+      grads(n_it - 1);
+      pre_g(n_it - 1);
+      __syncthreads();
+      matrix(n_it - 1, no, yes);  // dK(last)
+    }
+  }
+  if (key_ok) store_row<T, DB>((uint16_t*)(role == 0 ? p.dv : p.dk) + koff, acc,
+                               role == 0 ? 1.f : p.scale, hh);
+}
+
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   const int64_t dq_blocks = (int64_t)p.B * p.Hq * ((p.Nq + kDqRows - 1) / kDqRows);
@@ -675,8 +838,12 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
                      p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((int)kv_blocks), dim3(kBwdThreads), 0,
-                     st, p);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, D, CAUSAL>), dim3((int)kv_blocks),
+                       dim3(kPairThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((int)kv_blocks), dim3(kBwdThreads), 0,
+                       st, p);
   return hipGetLastError();
 }
 
