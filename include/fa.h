@@ -266,7 +266,8 @@ fa_status fa_kv_append(const void* k_new, const void* v_new, void* k_pool, void*
 
 /*
  * fa_bwd_workspace_size - bytes of device workspace that fa_bwd needs
- * (one float32 per query row and head). Returns 0 for invalid sizes.
+ * (two float32 per query row and head, rows rounded up to a multiple of
+ * 64). Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_size(int B, int Nq, int Hq);
 
@@ -287,7 +288,8 @@ size_t fa_bwd_workspace_size(int B, int Nq, int Hq);
  *     grouped-query heads, dk and dv of a key/value head sum the gradients
  *     of every query head that reads it
  *   workspace  at least fa_bwd_workspace_size(B, Nq, Hq) bytes of device
- *     memory owned by the caller (scratch: rowsum(dO o O) per row and head)
+ *     memory owned by the caller (scratch: rowsum(dO o O) and the LSE in
+ *     base 2 per row and head, laid out head by head)
  * B, Nq, Nk, Hq, Hkv >= 1 and a workspace of at least the stated size, else
  * FA_ERR_INVALID_ARG; dtype FA_F16 or FA_BF16 (FA_F32: FA_ERR_UNSUPPORTED);
  * causal masks as for fa_fwd (bottom-right). Two kernels on `stream`,

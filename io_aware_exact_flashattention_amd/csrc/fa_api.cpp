@@ -425,7 +425,8 @@ fa_status fa_decode_cascade(const void* q, const void* k_pool, const void* v_poo
 
 size_t fa_bwd_workspace_size(int B, int Nq, int Hq) {
   if (B <= 0 || Nq <= 0 || Hq <= 0) return 0;
-  return (size_t)B * Nq * Hq * sizeof(float);
+  const size_t n_pad = ((size_t)Nq + 63) / 64 * 64;
+  return 2 * (size_t)B * Hq * n_pad * sizeof(float);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -446,7 +447,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   fa::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
   p.dq = dq; p.dk = dk; p.dv = dv;
+  p.n_pad = (Nq + 63) / 64 * 64;
   p.dsum = static_cast<float*>(workspace);
+  p.lse2 = p.dsum + (size_t)B * Hq * p.n_pad;
   p.B = B; p.Nq = Nq; p.Nk = Nk; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
   p.q_row = (int64_t)Hq * d;
   p.kv_row = (int64_t)Hkv * d;

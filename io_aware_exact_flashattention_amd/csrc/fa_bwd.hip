@@ -311,7 +311,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdParams p) {
   }
   const float Dq = sum_halves(dpart);
   const float off = row_ok ? lse_offset(p.lse[tok * p.Hq + h]) : __builtin_inff();
-  if (row_ok && hh == 0) p.dsum[tok * p.Hq + h] = Dq;
+  // D and the lse offset of the row, head by head for the dK/dV kernels
+  // (their 64-row tiles then read one contiguous run)
+  if (row_ok && hh == 0) {
+    const int64_t ti = ((int64_t)b * p.Hq + h) * p.n_pad + my_row;
+    p.dsum[ti] = Dq;
+    p.lse2[ti] = off;
+  }
 
   int kv_end = Lk;
   if (CAUSAL) kv_end = min(Lk, row0 + kDqRows + delta);
@@ -455,9 +461,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
     Copy::issue((const uint16_t*)p.dout + base, p.q_row, q0, Lq, t0 + TB, wave, lane);
     if (tid < 2 * kKvRows) {
       const int row = q0 + (tid % kKvRows);
-      const int64_t li = ((int64_t)b * Lq + row) * p.Hq + h;
-      if (tid < kKvRows) sr = row < Lq ? lse_offset(p.lse[li]) : __builtin_inff();
-      else sr = row < Lq ? p.dsum[li] : 0.f;
+      const int64_t ti = ((int64_t)b * p.Hq + h) * p.n_pad + row;
+      if (tid < kKvRows) sr = row < Lq ? p.lse2[ti] : __builtin_inff();
+      else sr = row < Lq ? p.dsum[ti] : 0.f;
     }
   };
   // one 32-row block after the other
@@ -634,9 +640,9 @@ __global__ __launch_bounds__(kPairThreads) void bwd_dkdv_pair_kernel(BwdParams p
     }
     if (tid < 2 * kKvRows) {
       const int row = q0 + (tid % kKvRows);
-      const int64_t li = ((int64_t)b * Lq + row) * p.Hq + h;
-      if (tid < kKvRows) sr = row < Lq ? lse_offset(p.lse[li]) : __builtin_inff();
-      else sr = row < Lq ? p.dsum[li] : 0.f;
+      const int64_t ti = ((int64_t)b * p.Hq + h) * p.n_pad + row;
+      if (tid < kKvRows) sr = row < Lq ? p.lse2[ti] : __builtin_inff();
+      else sr = row < Lq ? p.dsum[ti] : 0.f;
     }
   };
   // barrier that ends slot it: tile it + 2 (issued one slot earlier) is

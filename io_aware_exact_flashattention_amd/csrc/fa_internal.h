@@ -89,7 +89,11 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* dsum;       // workspace: D = rowsum(dO o O) of every query row
+  // workspace, both [B, Hq, n_pad] float32 (rows padded to a multiple of 64
+  // so that a 64-row tile of one head is one contiguous run):
+  float* dsum;       // D = rowsum(dO o O) of every query row
+  float* lse2;       // log2-domain lse offset lse * log2(e) (+inf where lse = -inf)
+  int n_pad;         // Nq rounded up to a multiple of 64
   int B, Nq, Nk, Hq, Hkv, group;
   int64_t q_row;     // Hq * d
   int64_t kv_row;    // Hkv * d

@@ -223,5 +223,6 @@ def test_bwd_rejects(lib, kw, expect):
 
 
 def test_bwd_workspace_size(lib):
-    assert lib.fa_bwd_workspace_size(4, 2048, 16) == 4 * 2048 * 16 * 4
+    assert lib.fa_bwd_workspace_size(4, 2048, 16) == 2 * 4 * 2048 * 16 * 4
+    assert lib.fa_bwd_workspace_size(1, 65, 3) == 2 * 1 * 128 * 3 * 4  # rows padded to 64
     assert lib.fa_bwd_workspace_size(0, 2048, 16) == 0
