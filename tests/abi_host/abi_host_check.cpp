@@ -139,7 +139,8 @@ static void check_append() {
 
 static void check_bwd() {
   const size_t ws = fa_bwd_workspace_size(1, 16384, 32);
-  CHECK(ws == (size_t)16384 * 32 * 4);
+  CHECK(ws == (size_t)2 * 16384 * 32 * 4);  // D and the LSE offsets, rows padded to 64
+  CHECK(fa_bwd_workspace_size(2, 100, 3) == (size_t)2 * 2 * 3 * 128 * 4);
   auto call = [&](void* dq, size_t bytes, fa_dtype dt) {
     return fa_bwd(P, P, P, P, (float*)P, P, dq, P, P, 1, 16384, 16384, 32, 8, 128, dt, 0.088f, 1,
                   P, bytes, nullptr);
@@ -152,6 +153,7 @@ static void check_bwd() {
   CHECK(call(P, ws, FA_BF16) == FA_OK);
   CHECK(g_stub.last_kind == StubState::BWD && g_stub.bwd.group == 4 &&
         g_stub.bwd.q_row == 32 * 128 && g_stub.bwd.kv_row == 8 * 128 && g_stub.bwd.dsum == P);
+  CHECK(g_stub.bwd.n_pad == 16384 && g_stub.bwd.lse2 == (float*)P + (size_t)32 * 16384);
 }
 
 // ---- FA_DEBUG_VALIDATE: the stubbed copy reads these host arrays --------
