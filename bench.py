@@ -323,7 +323,7 @@ def other_configs(torch, fa, fi, to_dev, dev, reps=20):
         o, l = fa.fwd(q, k, v, causal=True, scale=x.scale)
         g_out = to_dev(fi.grad_out((B, Nq, Hq, d), x.dtype, 2), x.dtype)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        wsb = torch.empty(B * Nq * Hq * 4, dtype=torch.uint8, device=dev)
+        wsb = torch.empty(fa.bwd_workspace_size(B, Nq, Hq), dtype=torch.uint8, device=dev)
         mean, mn = timed(lambda: fa.bwd(q, k, v, o, l, g_out, causal=True, scale=x.scale, dq=dq,
                                         dk=dk, dv=dv, workspace=wsb))
         flops = 2.5 * fi.prefill_flops([Nq] * B, [Nk] * B, Hq, d, True)

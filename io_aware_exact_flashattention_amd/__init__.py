@@ -36,8 +36,8 @@ from . import _lib
 from ._lib import FaError
 
 __all__ = ["fwd", "fwd_varlen", "fwd_paged", "decode_paged", "decode_paged_noalloc",
-           "decode_cascade", "kv_append", "bwd", "decode_workspace_size", "FaError",
-           "default_scale"]
+           "decode_cascade", "kv_append", "bwd", "decode_workspace_size",
+           "bwd_workspace_size", "FaError", "default_scale"]
 
 _DT = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
 
@@ -248,6 +248,10 @@ def decode_workspace_size(B: int, Hq: int, d: int, max_pages: int, page_size: in
                           num_splits: int = 0) -> int:
     return int(_lib.load().fa_decode_paged_workspace_size(B, Hq, d, max_pages, page_size,
                                                           num_splits))
+
+
+def bwd_workspace_size(B: int, Nq: int, Hq: int) -> int:
+    return int(_lib.load().fa_bwd_workspace_size(B, Nq, Hq))
 
 
 def _decode_args(q, k_pool, v_pool, page_table, seq_lens):

@@ -214,7 +214,7 @@ def bwd(lib, **kw):
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(do=None), 1), (dict(dq=None), 1), (dict(dk=None), 1), (dict(dv=None), 1),
-    (dict(ws=None), 1), (dict(wsb=8 * 2 * 4 - 1), 1), (dict(o=None), 1), (dict(dq=40), 1),
+    (dict(ws=None), 1), (dict(wsb=2 * 2 * 64 * 4 - 1), 1), (dict(o=None), 1), (dict(dq=40), 1),
     (dict(B=0), 1), (dict(Nk=0), 1), (dict(Hq=3, Hkv=2), 1), (dict(dt=0), 2), (dict(d=96), 2),
     (dict(scale=float("nan")), 1),
 ])
