@@ -106,6 +106,18 @@ def test_backward_long_context_heads():
                     f"bwd long context head {h}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk,hq,hkv", [(5, 300, 2, 2), (64, 64, 1, 1), (65, 200, 1, 1),
+                                          (130, 130, 1, 1), (150, 500, 3, 3), (40, 40, 2, 1)])
+def test_backward_few_query_tiles(causal, nq, nk, hq, hkv):
+    """d=128 calls in which a key workgroup streams only one to four 64-row
+    Q/dO tiles (the prologue and the tail of the dK/dV tile pipeline carry
+    all the work), including a single row tile shared by two query heads."""
+    seed = 530 + nq + nk + hq
+    x = fi.dense(2, nq, nk, hq, hkv, 128, "bf16", seed=seed, causal=causal)
+    check_dense(x, f"bwd few tiles causal={causal} nq={nq} nk={nk} hq={hq} hkv={hkv}", seed)
+
+
 def test_backward_deterministic():
     x = fi.dense(1, 500, 500, 8, 2, 128, "bf16", seed=521, causal=True)
     q, k, v = dense_dev(x)
