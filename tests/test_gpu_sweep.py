@@ -88,7 +88,7 @@ def test_sweep_decode(case):
                num_splits=num_splits)
 
 
-@pytest.mark.parametrize("case", range(10))
+@pytest.mark.parametrize("case", range(20))
 def test_sweep_backward(case):
     rng = np.random.default_rng(9500 + case)
     B = int(rng.integers(1, 3))
