@@ -540,8 +540,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
 // SIMD. The "P wave" holds K, forms S = Q K^T and P and accumulates
 // dV^T += dO^T P; the "dS wave" holds V, forms dP = dO V^T and
 // dS = P o (dP - D) and accumulates dK^T += Q^T dS. P goes from the one to
-// the other through LDS in fp32, so every value is the one the single-wave
-// kernel computes. Each wave alternates a matrix phase (MFMAs and LDS
+// the other through LDS in fp32, so every value is the one that one wave
+// doing all of it would compute (as bwd_dkdv_kernel does at d = 64). Each wave alternates a matrix phase (MFMAs and LDS
 // fragment reads) with a vector phase (P, or dS), the two waves of a SIMD in
 // counter-phase, every phase boundary a workgroup barrier, as in the forward
 // kernel:
@@ -687,7 +687,7 @@ __global__ __launch_bounds__(kPairThreads) void bwd_dkdv_pair_kernel(BwdParams p
   // product of tile it (GRAD), one MFMA of each per step; A fragments are
   // read two steps ahead. Score MFMA i: block i / KS, k-step i % KS.
   // Gradient MFMA i: block i / (2 DB), d-block (i % (2 DB)) / 2, rows
-  // 16 (i % 2) of the block (the order of the single-wave kernel).
+  // 16 (i % 2) of the block (the order in which bwd_dkdv_kernel accumulates).
   // score A operand rows: Q (P wave) or dO (dS wave) of tile it + 1;
   // gradient A operand: dO (P wave) or Q (dS wave) of tile it, transposed
   auto sfrag = [&](int it, int i) {
