@@ -30,8 +30,8 @@
 //    forward kernel's wave pairs. At d = 64 (bwd_dkdv_kernel) one wave does
 //    all of it for its 32 keys, so that two workgroups fit on a CU.
 // Work items are numbered so that each XCD runs a contiguous stretch of the
-// work list: the items running on one XCD at a time read the same Q/dO (or
-// K/V) tiles, which then stay in its L2.
+// work list, longest tiles of its heads first: the items running on one XCD
+// at a time read the same Q/dO (or K/V) tiles, which then stay in its L2.
 // Tiles reach LDS by direct-to-LDS copies; S and dP live in VGPRs, the
 // gradient accumulators in AGPRs or VGPRs (inline-asm MFMAs with fixed
 // register classes and explicit waits).
@@ -230,14 +230,26 @@ __device__ __forceinline__ float dot8(uint4 a, uint4 b) {
   return s;
 }
 
-// Workgroups are dealt round-robin over the 8 XCDs (workgroup L runs on
-// XCD L % 8); this renumbering gives XCD x the contiguous range
-// [x*per + min(x, rem), ...) of the work list, so that the items running on
-// one XCD at a time are neighbours in the list and share tiles in its L2.
-__device__ __forceinline__ int xcd_item() {
+// Work order. Workgroups are dealt round-robin over the 8 XCDs (workgroup L
+// runs on XCD L % 8), so the ids are renumbered: XCD x takes the contiguous
+// stretch [x*per + min(x, rem), ...) of the work list of (sequence, head)
+// units of n_tiles items each, and the items running on one XCD at a time
+// share the units' tiles in its L2. When the stretch is made of whole units
+// it is taken tile-major - the first tile of each of its units, then the
+// second, and so on - so that its longest items (under a causal mask) start
+// first on every unit. Returns the unit and the tile rank.
+__device__ __forceinline__ void xcd_unit_tile(int n_tiles, int& unit, int& rank) {
   const int L = blockIdx.x, total = gridDim.x;
-  const int xcd = L & 7, per = total >> 3, rem = total & 7;
-  return xcd * per + min(xcd, rem) + (L >> 3);
+  const int xcd = L & 7, idx = L >> 3, per = total >> 3, rem = total & 7;
+  if (rem == 0 && per % n_tiles == 0) {
+    const int upx = per / n_tiles;
+    unit = xcd * upx + idx % upx;
+    rank = idx / upx;
+  } else {
+    const int item = xcd * per + min(xcd, rem) + idx;
+    unit = item / n_tiles;
+    rank = item % n_tiles;
+  }
 }
 
 // lse (natural log) -> the log2-domain offset of P = exp2(s * scale_log2 -
@@ -276,9 +288,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdParams p) {
 
   // work item (sequence b, query head h, query tile t), longest causal tiles first
   const int nt = (p.Nq + kDqRows - 1) / kDqRows;
-  int idx = xcd_item();
-  const int t = nt - 1 - idx % nt;
-  idx /= nt;
+  int idx, rank;
+  xcd_unit_tile(nt, idx, rank);
+  const int t = nt - 1 - rank;
   const int h = idx % p.Hq, b = idx / p.Hq;
   const int g = h / p.group;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -405,9 +417,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
   // work item (sequence b, key/value head g, key tile t); under a causal
   // mask the first key tiles see the most queries and come first
   const int nt = (p.Nk + kKvKeys - 1) / kKvKeys;
-  int idx = xcd_item();
-  const int t = idx % nt;
-  idx /= nt;
+  int idx, t;
+  xcd_unit_tile(nt, idx, t);
   const int g = idx % p.Hkv, b = idx / p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -570,9 +581,8 @@ __global__ __launch_bounds__(kPairThreads) void bwd_dkdv_pair_kernel(BwdParams p
   __shared__ __attribute__((aligned(16))) float4 xch[4][8][64];
 
   const int nt = (p.Nk + kKvKeys - 1) / kKvKeys;
-  int idx = xcd_item();
-  const int t = idx % nt;
-  idx /= nt;
+  int idx, t;
+  xcd_unit_tile(nt, idx, t);
   const int g = idx % p.Hkv, b = idx / p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
