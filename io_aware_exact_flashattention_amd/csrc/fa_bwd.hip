@@ -403,7 +403,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdParams p) {
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
-  static_assert(D == 64, "d = 128 runs bwd_dkdv_pair_kernel");
+  static_assert(D == 64, "d = 128 always runs bwd_dkdv_pair_kernel");
   using E = Elem<T>;
   using G = Tile<D>;
   constexpr int KS = D / 16;
@@ -562,6 +562,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdParams p) {
 // barrier that ends slot i-2 completes it, the one that ends slot i-3 issues
 // its copies into a ring of three buffers.
 constexpr int kPairThreads = 512;  // 4 key groups x 2 roles
+constexpr int kCUs = 256;          // compute units of an MI355X
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kPairThreads) void bwd_dkdv_pair_kernel(BwdParams p) {
@@ -854,12 +855,21 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
                      p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (D == 128)
+  // d = 128: always the wave-pair kernel. d = 64: the one-wave kernel, whose
+  // two workgroups per CU fill the chip when there are enough of them; with
+  // fewer key workgroups than CUs the wave-pair kernel's eight waves per
+  // workgroup do more. Both give the same bits.
+  if constexpr (D == 128) {
     hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, D, CAUSAL>), dim3((int)kv_blocks),
                        dim3(kPairThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((int)kv_blocks), dim3(kBwdThreads), 0,
-                       st, p);
+  } else {
+    if (kv_blocks < kCUs)
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, D, CAUSAL>), dim3((int)kv_blocks),
+                         dim3(kPairThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((int)kv_blocks), dim3(kBwdThreads),
+                         0, st, p);
+  }
   return hipGetLastError();
 }
 
